@@ -1,0 +1,160 @@
+"""Exact scaled-dot-product attention forward for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libattn.so`` (see ``include/attn.h``).  The
+functions carry the C names and only marshal arguments: torch tensors supply device
+pointers and the current HIP stream, and every step of the computation runs in the HIP
+kernels.  There is no fallback: if the library is not built, or a call is refused, an
+exception is raised.
+
+    o, lse = attn_fwd(q, k, v, scale=None, causal=False)
+    ws = attn_fwd_splitkv(q, k, v, num_splits, ...)
+    o, lse = attn_merge(ws, num_splits, B, H, Sq, d)
+
+Tensors are [B, H, S, d] contiguous on the GPU: torch.float32, torch.bfloat16, or FP8
+E4M3FN codes (torch.float8_e4m3fn, or torch.uint8 holding the codes).  Outputs are
+float32.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3, ATTN_MAX_SPLITS, AttnError  # noqa: F401
+
+__all__ = [
+    "attn_fwd", "attn_fwd_splitkv", "attn_merge", "attn_splitkv_workspace_bytes",
+    "attn_block_m", "attn_block_n", "attn_num_workgroups", "attn_kernel_name",
+    "attn_status_string", "attn_last_hip_error", "dtype_code", "library_path", "AttnError",
+]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return ATTN_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def ctypes_ptr(t: torch.Tensor) -> int:
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _qkv(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, d]")
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    if tuple(k.shape) != (B, H, Sk, d) or tuple(v.shape) != (B, H, Sk, d):
+        raise ValueError("k and v must be [B, H, Sk, d] with q's B, H and d")
+    dt = dtype_code(q)
+    if dtype_code(k) != dt or dtype_code(v) != dt:
+        raise TypeError("q, k and v must share one dtype")
+    return B, H, Sq, Sk, d, dt
+
+
+def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """O = softmax(scale * Q K^T [causal mask]) V and the row log-sum-exp, both fp32."""
+    B, H, Sq, Sk, d, dt = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Sq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    st = _lib.load().attn_fwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out),
+                              ctypes_ptr(lse), B, H, Sq, Sk, d, float(scale), int(causal), dt,
+                              _stream(stream))
+    _lib.check("attn_fwd", st)
+    return out, lse
+
+
+def attn_splitkv_workspace_bytes(B, H, Sq, d, num_splits) -> int:
+    return int(_lib.load().attn_splitkv_workspace_bytes(B, H, Sq, d, num_splits))
+
+
+def attn_fwd_splitkv(q, k, v, num_splits, scale=None, causal=False, descales=(1.0, 1.0, 1.0),
+                     ws=None, stream=None):
+    """Per-chunk softmax states (m, l, u) of an n-way key split, in a workspace tensor."""
+    B, H, Sq, Sk, d, dt = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = attn_splitkv_workspace_bytes(B, H, Sq, d, num_splits)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    qd, kd, vd = (float(x) for x in descales)
+    st = _lib.load().attn_fwd_splitkv(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(ws),
+                                      ws.numel() * ws.element_size(), int(num_splits), B, H, Sq,
+                                      Sk, d, float(scale), int(causal), dt, qd, kd, vd,
+                                      _stream(stream))
+    _lib.check("attn_fwd_splitkv", st)
+    return ws
+
+
+def attn_merge(ws, num_splits, B, H, Sq, d, out=None, lse=None, stream=None):
+    """Combine the chunk states of ``ws`` into (O, lse)."""
+    dev = ws.device
+    if out is None:
+        out = torch.empty((B, H, Sq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    st = _lib.load().attn_merge(ctypes_ptr(ws), ws.numel() * ws.element_size(), int(num_splits),
+                                ctypes_ptr(out), ctypes_ptr(lse), B, H, Sq, d, _stream(stream))
+    _lib.check("attn_merge", st)
+    return out, lse
+
+
+def workspace_views(ws, num_splits, B, H, Sq, d):
+    """(m, l, u) views of a split-KV workspace, shaped [n,B,H,Sq], [n,B,H,Sq], [n,B,H,Sq,d]."""
+    rows = B * H * Sq
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    ml = num_splits * rows * 4
+    f = ws.view(torch.uint8)
+    m = f[0:ml].view(torch.float32).view(num_splits, B, H, Sq)
+    l_off = up(ml)
+    l = f[l_off:l_off + ml].view(torch.float32).view(num_splits, B, H, Sq)
+    u_off = l_off + up(ml)
+    u = f[u_off:u_off + ml * d].view(torch.float32).view(num_splits, B, H, Sq, d)
+    return m, l, u
+
+
+def attn_block_m(d, dtype):
+    return int(_lib.load().attn_block_m(d, dtype))
+
+
+def attn_block_n(d, dtype):
+    return int(_lib.load().attn_block_n(d, dtype))
+
+
+def attn_num_workgroups(B, H, Sq, d, dtype, num_splits=1):
+    return int(_lib.load().attn_num_workgroups(B, H, Sq, d, dtype, num_splits))
+
+
+def attn_kernel_name(d, dtype, splitkv=False):
+    return _lib.load().attn_kernel_name(d, dtype, int(bool(splitkv))).decode()
+
+
+def attn_status_string(status):
+    return _lib.load().attn_status_string(status).decode()
+
+
+def attn_last_hip_error():
+    return int(_lib.load().attn_last_hip_error())

@@ -1,0 +1,175 @@
+// C ABI of the attention library: argument checks, workspace layout and dispatch.
+//
+// Every check runs before anything is launched, so a refused call has no effect on the
+// outputs.  Nothing in this file touches the GPU; the launches live in
+// attn_kernels.hip.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr double kLog2e = 1.4426950408889634073599246810019;
+constexpr int64_t kMaxIndex = int64_t(1) << 46;  // element counts addressed with 64-bit offsets
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
+bool supported_dtype(int t) { return t == ATTN_F32 || t == ATTN_BF16 || t == ATTN_FP8_E4M3; }
+bool positive_finite(float x) { return std::isfinite(x) && x > 0.0f; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape checks common to the forward entry points.
+attn_status check_shape(int B, int H, int Sq, int Sk, int d, int dtype) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ATTN_ERR_SHAPE;
+  if (!supported_d(d) || !supported_dtype(dtype)) return ATTN_ERR_UNSUPPORTED;
+  const int64_t bh = int64_t(B) * H;
+  if (bh * Sq * d >= kMaxIndex || bh * Sk * d >= kMaxIndex) return ATTN_ERR_SHAPE;
+  if (bh * ceil_div(Sq, attn::kBlockM) >= (int64_t(1) << 31) / ATTN_MAX_SPLITS) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+attn_status launched(int hip_err) {
+  if (hip_err != 0) {
+    g_last_hip_error = hip_err;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+                     int B, int H, int Sq, int Sk, int d, float scale, int causal,
+                     attn_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  attn_status st = check_shape(B, H, Sq, Sk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  if ((causal != 0 && causal != 1) || !positive_finite(scale)) return ATTN_ERR_ARG;
+  const float sl2 = static_cast<float>(double(scale) * kLog2e);
+  if (!positive_finite(sl2)) return ATTN_ERR_ARG;
+
+  attn::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.dtype = dtype; a.causal = causal;
+  a.num_splits = 1; a.chunk = Sk; a.split_mode = 0;
+  a.scale_log2 = sl2;
+  a.v_scale = 1.0f;
+  return launched(attn::launch_fwd(a, stream));
+}
+
+size_t attn_splitkv_workspace_bytes(int B, int H, int Sq, int d, int num_splits) {
+  if (B < 1 || H < 1 || Sq < 1 || !supported_d(d)) return 0;
+  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return 0;
+  const int64_t rows = int64_t(B) * H * Sq;
+  if (rows * d >= kMaxIndex) return 0;
+  return attn::workspace_layout(rows, d, num_splits).total;
+}
+
+attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v,
+                             void* ws, size_t ws_bytes, int num_splits,
+                             int B, int H, int Sq, int Sk, int d, float scale, int causal,
+                             attn_dtype dtype, float q_descale, float k_descale,
+                             float v_descale, void* stream) {
+  if (!q || !k || !v || !ws) return ATTN_ERR_NULL;
+  attn_status st = check_shape(B, H, Sq, Sk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(ws)) return ATTN_ERR_ALIGN;
+  if ((causal != 0 && causal != 1) || !positive_finite(scale) || !positive_finite(q_descale) ||
+      !positive_finite(k_descale) || !positive_finite(v_descale))
+    return ATTN_ERR_ARG;
+  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
+  const float sl2 =
+      static_cast<float>(double(scale) * double(q_descale) * double(k_descale) * kLog2e);
+  if (!positive_finite(sl2)) return ATTN_ERR_ARG;
+  const int64_t rows = int64_t(B) * H * Sq;
+  const attn::WorkspaceLayout w = attn::workspace_layout(rows, d, num_splits);
+  if (ws_bytes < w.total) return ATTN_ERR_WORKSPACE;
+
+  char* base = static_cast<char*>(ws);
+  attn::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.ws_m = reinterpret_cast<float*>(base + w.m_off);
+  a.ws_l = reinterpret_cast<float*>(base + w.l_off);
+  a.ws_u = reinterpret_cast<float*>(base + w.u_off);
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.dtype = dtype; a.causal = causal;
+  a.num_splits = num_splits;
+  a.chunk = static_cast<int>(ceil_div(Sk, num_splits));
+  a.split_mode = 1;
+  a.scale_log2 = sl2;
+  a.v_scale = v_descale;
+  return launched(attn::launch_fwd(a, stream));
+}
+
+attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o, float* lse,
+                       int B, int H, int Sq, int d, void* stream) {
+  if (!ws || !o || !lse) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || Sq < 1) return ATTN_ERR_SHAPE;
+  if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(ws) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
+  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
+  const int64_t rows = int64_t(B) * H * Sq;
+  if (rows * d >= kMaxIndex) return ATTN_ERR_SHAPE;
+  const attn::WorkspaceLayout w = attn::workspace_layout(rows, d, num_splits);
+  if (ws_bytes < w.total) return ATTN_ERR_WORKSPACE;
+
+  const char* base = static_cast<const char*>(ws);
+  attn::MergeArgs a{};
+  a.ws_m = reinterpret_cast<const float*>(base + w.m_off);
+  a.ws_l = reinterpret_cast<const float*>(base + w.l_off);
+  a.ws_u = reinterpret_cast<const float*>(base + w.u_off);
+  a.o = o; a.lse = lse;
+  a.rows = rows; a.d = d; a.num_splits = num_splits;
+  return launched(attn::launch_merge(a, stream));
+}
+
+int attn_block_m(int d, attn_dtype dtype) {
+  if (!supported_d(d) || !supported_dtype(dtype)) return 0;
+  return attn::kBlockM;
+}
+
+int attn_block_n(int d, attn_dtype dtype) {
+  if (!supported_d(d) || !supported_dtype(dtype)) return 0;
+  return attn::block_n(dtype, d);
+}
+
+int64_t attn_num_workgroups(int B, int H, int Sq, int d, attn_dtype dtype, int num_splits) {
+  if (B < 1 || H < 1 || Sq < 1 || !supported_d(d) || !supported_dtype(dtype)) return -1;
+  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return -1;
+  return int64_t(B) * H * ceil_div(Sq, attn::kBlockM) * num_splits;
+}
+
+const char* attn_kernel_name(int d, attn_dtype dtype, int splitkv) {
+  if (!supported_d(d) || !supported_dtype(dtype)) return "unsupported";
+  return attn::fwd_kernel_name(dtype, d, splitkv ? 1 : 0);
+}
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "B, H, Sq and Sk must be >= 1 and the tensors indexable";
+    case ATTN_ERR_ALIGN: return "pointers must be 16-byte aligned";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dim (64, 128, 256) or dtype";
+    case ATTN_ERR_WORKSPACE: return "split-KV workspace too small";
+    case ATTN_ERR_HIP: return "HIP kernel launch failed";
+    case ATTN_ERR_ARG: return "causal must be 0/1; scale and descales finite and > 0; "
+                              "1 <= num_splits <= ATTN_MAX_SPLITS";
+  }
+  return "unknown status";
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

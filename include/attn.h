@@ -1,0 +1,160 @@
+/*
+ * attn.h -- C ABI of the exact scaled-dot-product attention forward library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (defined on the pages "AI 大模型之 FlashAttention_02", sections 3.1 and
+ * 4.1, and "Inside FlashAttention-3", section 2) is, for every batch b and head h,
+ *
+ *     S   = scale * Q K^T                      (Sq x Sk, never stored)
+ *     S_ij = -inf where key j is masked
+ *     O   = softmax(S) V,   lse_i = ln sum_j exp(S_ij)
+ *
+ * computed tile by tile with the two-level online softmax (running row maximum m,
+ * running sum l, rescale factor exp(m_old - m_new), division by l deferred to the
+ * write-back), so that the score matrix never reaches device memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout     Q is [B, H, Sq, d]; K and V are [B, H, Sk, d]; O is [B, H, Sq, d] fp32;
+ *             lse is [B, H, Sq] fp32.  All contiguous, row-major, in device memory.
+ *  Types      ATTN_F32: float; ATTN_BF16: bfloat16 bit patterns (uint16);
+ *             ATTN_FP8_E4M3: OCP FP8 E4M3FN codes (uint8, bias 7, max 448, no inf).
+ *  Alignment  every pointer must be 16-byte aligned.
+ *  Head dim   d must be 64, 128 or 256.  Anything else is refused (no fallback).
+ *  Masks      causal = 0: none.  causal = 1: key j is hidden from query i when
+ *             j > i + (Sk - Sq) (aligned to the bottom-right corner; the usual j > i
+ *             when Sq == Sk).  A query row that sees no key gets O = 0, lse = -inf.
+ *  scale      applied as the given fp32 value; must be finite and > 0.
+ *  lse        natural log of the sum of exp of the row's visible scaled scores.
+ *  Streams    `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *             asynchronous on that stream; results are valid once the stream has
+ *             reached that point.  The library never allocates, frees or
+ *             synchronises; the caller owns every buffer and keeps it alive until
+ *             the stream is done with it.  Calls are thread-safe.
+ *  Errors     every call returns an attn_status.  All arguments are checked before
+ *             anything is launched, so a refused call leaves every output untouched.
+ *             A failed launch returns ATTN_ERR_HIP and records the HIP error code,
+ *             readable with attn_last_hip_error() on the calling thread.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_F32 = 0,
+  ATTN_BF16 = 1,
+  ATTN_FP8_E4M3 = 2
+} attn_dtype;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL                              */
+  ATTN_ERR_SHAPE = 2,       /* B, H, Sq or Sk < 1, or sizes too large to index         */
+  ATTN_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                         */
+  ATTN_ERR_UNSUPPORTED = 4, /* head dim or dtype not supported                          */
+  ATTN_ERR_WORKSPACE = 5,   /* split-KV workspace smaller than attn_splitkv_workspace_bytes */
+  ATTN_ERR_HIP = 6,         /* the kernel launch failed (see attn_last_hip_error)      */
+  ATTN_ERR_ARG = 7          /* causal not 0/1, scale or a descale not finite and > 0,
+                               num_splits out of [1, ATTN_MAX_SPLITS]                  */
+} attn_status;
+
+#define ATTN_MAX_SPLITS 4096
+
+/*
+ * attn_fwd -- fused attention forward: O and lse for every (b, h, query row).
+ *
+ * One workgroup per (b, h, tile of query rows) sweeps all visible keys (the
+ * sequence-level work partition of "AI 大模型之 FlashAttention_02", section "From
+ * head-level to sequence-level parallelism"); no workgroup ever reduces with another.
+ * For ATTN_FP8_E4M3 the codes are used as they are: fold any q/k descale into
+ * `scale` and multiply O by the v descale afterwards (attn_fwd_splitkv takes the
+ * descales explicitly).
+ *
+ *   q, k, v   device pointers, layout and type as above (read only)
+ *   o, lse    device pointers, fp32 outputs (written completely)
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+                     int B, int H, int Sq, int Sk, int d, float scale, int causal,
+                     attn_dtype dtype, void* stream);
+
+/*
+ * attn_splitkv_workspace_bytes -- bytes of the workspace attn_fwd_splitkv writes and
+ * attn_merge reads for this shape, or 0 if an argument is out of range.
+ *
+ * Workspace layout (all fp32, each section starting at a multiple of 256 bytes from
+ * the workspace base), with R = B*H*Sq rows and n = num_splits:
+ *     m [n][B][H][Sq]   chunk maximum of the scaled scores, natural-log units (-inf: empty)
+ *     l [n][B][H][Sq]   sum over the chunk of exp(S - m)
+ *     u [n][B][H][Sq][d] sum over the chunk of exp(S - m) * v * v_descale (not divided by l)
+ */
+size_t attn_splitkv_workspace_bytes(int B, int H, int Sq, int d, int num_splits);
+
+/*
+ * attn_fwd_splitkv -- local softmax states of an n-way split of the keys.
+ *
+ * The key axis is cut into n chunks of C = ceil(Sk / n) keys: chunk s covers keys
+ * [s*C, min(Sk, (s+1)*C)); chunks past the end are empty and get the neutral state
+ * (m = -inf, l = 0, u = 0).  Each chunk's (m, l, u) is written to the workspace as
+ * laid out above (the split-K scheme and worked example of "AI 大模型之
+ * FlashAttention_02", section "Engineering practice: reduction along keys vs. along
+ * queries").  Combine with attn_merge.
+ *
+ *   ws, ws_bytes          device workspace and its size in bytes (>= the size above)
+ *   num_splits            n, 1 <= n <= ATTN_MAX_SPLITS
+ *   q_descale, k_descale  fp32 factors applied to the scores: S = scale*qd*kd*(Q K^T)
+ *   v_descale             fp32 factor applied to V (it ends up in u)
+ *   (use 1.0 for all three unless the inputs are scaled FP8 codes)
+ */
+attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v,
+                             void* ws, size_t ws_bytes, int num_splits,
+                             int B, int H, int Sq, int Sk, int d, float scale, int causal,
+                             attn_dtype dtype, float q_descale, float k_descale,
+                             float v_descale, void* stream);
+
+/*
+ * attn_merge -- combine the n chunk states of a workspace into O and lse.
+ *
+ * With M = max_s m_s and w_s = exp(m_s - M) (0 for an empty chunk):
+ * L = sum_s w_s l_s, O = sum_s w_s u_s / L, lse = M + ln L; a row whose chunks are all
+ * empty gets O = 0, lse = -inf.  This is the merge of the split-K section of
+ * "AI 大模型之 FlashAttention_02" (each chunk rescaled to the global maximum before
+ * summing, normalised once).
+ *
+ *   ws, ws_bytes   workspace written by attn_fwd_splitkv with the same shape and n
+ *   o, lse         device pointers, fp32 outputs [B,H,Sq,d] and [B,H,Sq]
+ */
+attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o, float* lse,
+                       int B, int H, int Sq, int d, void* stream);
+
+/* Query rows per workgroup that attn_fwd / attn_fwd_splitkv use for (d, dtype), or 0. */
+int attn_block_m(int d, attn_dtype dtype);
+
+/* Keys per tile of the key sweep for (d, dtype), or 0 if unsupported. */
+int attn_block_n(int d, attn_dtype dtype);
+
+/*
+ * Number of workgroups one launch uses: B * H * ceil(Sq / block_m) * num_splits
+ * (num_splits = 1 for attn_fwd), or -1 if an argument is out of range.
+ */
+int64_t attn_num_workgroups(int B, int H, int Sq, int d, attn_dtype dtype, int num_splits);
+
+/* Name of the kernel instance a call with these arguments launches (static string). */
+const char* attn_kernel_name(int d, attn_dtype dtype, int splitkv);
+
+/* Human-readable text of a status code (static string). */
+const char* attn_status_string(attn_status s);
+
+/* HIP error code of the last failed launch on the calling thread (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */
