@@ -1,0 +1,232 @@
+"""Benchmark of the exact attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+Workload (default): B=1, H=8, Sq=Sk=8192, d=128, Q/K/V i.i.d. N(0,1) rounded to bf16,
+scale 1/sqrt(d).  One step is one forward pass of the whole path over that batch in
+both mask modes: non-causal, then causal (two launches of the same kernel).  Inputs
+are resident in device memory before the timed region.  Throughput counts
+4*B*H*Sq*Sk*d FLOPs per non-causal pass and half of that per causal pass.
+
+Prints one JSON line.  Besides the headline throughput it carries
+  roofline      the kernel's achieved TFLOP/s from HIP events around every launch in
+                the timed region, against the bf16 dense MFMA peak; `traffic` is the
+                HBM bytes per launch measured by rocprofv3 counters (profiles/), or
+                null when that measurement does not match the current kernel source;
+  cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample.
+A few sampled rows are checked against the oracle outside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_82_amd", "csrc", "attn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_attn_fwd_bf16_d128_B1_H8_S8192.txt")
+
+WORKLOADS = {
+    # name: (B, H, S, d, seed)
+    "c3": (1, 8, 8192, 128, 3),
+    "c2": (8, 32, 2048, 64, 2),
+}
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, if it matches the source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, scale, budget_s: float):
+    """Time the fp64 oracle on whole heads of the same workload, both masks, until the
+    budget is used (at least one head per mask)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    B, H, S, d = inp.B, inp.H, inp.Sq, inp.d
+    q = inp.q64.reshape(B * H, S, d)
+    k = inp.k64.reshape(B * H, S, d)
+    v = inp.v64.reshape(B * H, S, d)
+    flops = 0.0
+    heads = 0
+    t0 = time.perf_counter()
+    while True:
+        h = heads % (B * H)
+        for causal in (False, True):
+            oracle.attention(q[h], k[h], v[h], scale, causal)
+            flops += oracle.flops(1, 1, S, S, d, causal)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s or heads >= B * H:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} head(s) of B={B},H={H},S={S},d={d} bf16 inputs, non-causal and "
+                      f"causal each, fp64 NumPy oracle (full score matrix), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_82_amd as ea
+    import synthetic_inputs as si
+
+    B, H, S, d, seed = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = si.make_attention_inputs(B, H, S, S, d, seed=seed, dtype="bf16")
+    q, k, v = (torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).to(dev)
+               for t in (inp.q, inp.k, inp.v))
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    o = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    modes = (False, True)
+    flops = {c: 4.0 * B * H * S * S * d / (2.0 if c else 1.0) for c in modes}
+
+    def step(events=None):
+        for i, c in enumerate(modes):
+            if events is not None:
+                events[i][0].record()
+            ea.attn_fwd(q, k, v, scale=scale, causal=c, out=o, lse=lse)
+            if events is not None:
+                events[i][1].record()
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in modes] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_mode_ms = {c: [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+                   for i, c in enumerate(modes)}
+    ms_step = wall * 1e3 / args.steps
+    total_flops = sum(flops.values())
+    value = total_flops * args.steps / wall / 1e12
+    kern_ms = float(np.mean([np.mean(per_mode_ms[c]) for c in modes]))
+    kern_flops = total_flops / len(modes)
+    achieved = kern_flops / (kern_ms * 1e-3) / 1e12
+
+    # numerics, outside the timed region: sampled rows of two heads vs the oracle
+    import oracle
+    rows = np.array([0, 1, 127, 128, S // 2, S - 129, S - 1])
+    worst = 0.0
+    for c in modes:
+        ea.attn_fwd(q, k, v, scale=scale, causal=c, out=o, lse=lse)
+        og = o.cpu().numpy().reshape(B * H, S, d)
+        for h in (0, B * H - 1):
+            ro, _ = oracle.attention(inp.q64.reshape(B * H, S, d)[h][rows],
+                                     inp.k64.reshape(B * H, S, d)[h],
+                                     inp.v64.reshape(B * H, S, d)[h], scale, c,
+                                     Sq_total=S, q_index=rows)
+            worst = max(worst, float(np.abs(og[h][rows] - ro).max()))
+    if worst > 1e-2:
+        print(f"numerics check failed: max|dO| = {worst}", file=sys.stderr)
+        sys.exit(1)
+
+    traffic = read_traffic() if args.workload == "c3" else None
+    result = {
+        "metric": "attention fwd TFLOPS (bf16, causal/non-causal) and % of MI355X MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: B={B}, H={H}, Sq=Sk={S}, d={d}, bf16 N(0,1) inputs, "
+                        "fp32 O + lse; one step = non-causal + causal forward",
+            "B": B, "H": H, "Sq": S, "Sk": S, "d": d, "masks": ["non-causal", "causal"],
+            "kernel": ea.attn_kernel_name(d, ea.ATTN_BF16),
+        },
+        "modes": {
+            ("causal" if c else "non_causal"): {
+                "tflops": round(flops[c] / (np.median(per_mode_ms[c]) * 1e-3) / 1e12, 2),
+                "median_us": round(float(np.median(per_mode_ms[c])) * 1e3, 2),
+                "p10_us": round(float(np.percentile(per_mode_ms[c], 10)) * 1e3, 2),
+                "p90_us": round(float(np.percentile(per_mode_ms[c], 90)) * 1e3, 2),
+                "pct_bf16_peak": round(100.0 * flops[c] / (np.median(per_mode_ms[c]) * 1e-3)
+                                       / 1e12 / PEAK_BF16_TFLOPS, 2),
+            } for c in modes
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "numerics_max_abs_err_sampled": worst,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, scale, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
