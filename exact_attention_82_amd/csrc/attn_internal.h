@@ -9,12 +9,13 @@ namespace attn {
 
 // Tile geometry shared by the dispatcher and the kernels.
 constexpr int kThreads = 256;     // 4 wavefronts of 64 lanes
+constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;  // query rows owned by one wavefront
 constexpr int kBlockM = 128;      // query rows per workgroup
 
 // Keys per tile of the key sweep, by element type and head dim.
-constexpr int block_n(int dtype, int /*d*/) {
-  return dtype == 0 ? 32 : 64;  // fp32: 32; bf16, fp8: 64
+constexpr int block_n(int dtype, int d) {
+  return dtype == 0 ? 32 : dtype == 1 ? (d == 64 ? 64 : 32) : 64;  // fp32 | bf16 | fp8
 }
 
 struct FwdArgs {

@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_internal.h"
 
 namespace attn {
@@ -65,28 +67,25 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // ------------------------------------------------------------------ element traits
 // kKPL: contraction elements one lane supplies per MFMA; kKS: contraction depth of one
-// MFMA (two lane halves); kTau: lazy-rescale threshold in log2 units.
+// MFMA (two lane halves); kTau: lazy-rescale threshold in log2 units; kDMA: tiles
+// reach LDS by direct buffer-to-LDS loads (else through registers).
 template <int DT> struct Traits;
 
 template <> struct Traits<DT_BF16> {
   using Op = bf16x8_t;
   static constexpr int kBytes = 2, kKPL = 8, kKS = 16;
-  static constexpr bool kVT = true;  // value tile stored transposed in LDS
-  static constexpr int kKPad = 16, kVPad = 16;
+  static constexpr bool kDMA = true;
   static constexpr float kTau = 8.0f;
   static constexpr float kPScale = 1.0f;
   __device__ static f32x16_t mfma(Op a, Op b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  __device__ static Op load(const void* p) { return *reinterpret_cast<const Op*>(p); }
-  __device__ static Op zero() { return Op{}; }
 };
 
 template <> struct Traits<DT_FP8> {
   using Op = long;
   static constexpr int kBytes = 1, kKPL = 8, kKS = 16;
-  static constexpr bool kVT = true;
-  static constexpr int kKPad = 8, kVPad = 8;
+  static constexpr bool kDMA = true;
   // FP8 probabilities are scaled by 2^8 before rounding to E4M3 (max 448) so that
   // they sit in the format's normal range; the exact rescale keeps them <= 1 first.
   static constexpr float kTau = 0.0f;
@@ -94,233 +93,446 @@ template <> struct Traits<DT_FP8> {
   __device__ static f32x16_t mfma(Op a, Op b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, c, 0, 0, 0);
   }
-  __device__ static Op load(const void* p) { return *reinterpret_cast<const long*>(p); }
-  __device__ static Op zero() { return 0; }
 };
 
 template <> struct Traits<DT_F32> {
   using Op = float;
   static constexpr int kBytes = 4, kKPL = 1, kKS = 2;
-  static constexpr bool kVT = false;  // value tile kept as [key][d]
-  static constexpr int kKPad = 4, kVPad = 16;
+  static constexpr bool kDMA = false;
   static constexpr float kTau = 8.0f;
   static constexpr float kPScale = 1.0f;
   __device__ static f32x16_t mfma(Op a, Op b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
-  __device__ static Op load(const void* p) { return *reinterpret_cast<const float*>(p); }
-  __device__ static Op zero() { return 0.0f; }
 };
 
-// ------------------------------------------------------------------ tile geometry
-template <int DT, int D, int BN> struct Geo {
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+// Raw buffer loads return zero past num_records, so rows at or beyond the sequence
+// end read as zeros without any branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Workgroup barrier without the release fence of __syncthreads(): the fence would make
+// the compiler wait for every direct-to-LDS load still in flight (vmcnt(0)), including
+// the ones meant to stay in flight across the barrier.  Callers wait explicitly for
+// the loads whose data must be visible; LDS writes from registers are drained here
+// (lgkmcnt(0)); the empty asm statements stop the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ================================================================== direct-to-LDS tiles
+// A key or value tile (BN rows of D elements) lands in LDS row-major without padding;
+// bank conflicts are avoided by XOR-permuting the 16-byte chunks of each row.
+//
+// Key tile: the S^T MFMA reads one 16-byte (bf16) or 8-byte (fp8) piece per lane,
+// 16 consecutive rows at the same column; the key swizzle gives those rows distinct
+// banks.  Value tile (bf16): the transposed LDS read (ds_read_b64_tr_b16) has each
+// 16-lane group fetch 4 consecutive rows x 32 bytes; the value swizzle puts the 4 rows
+// of a group, and the two groups sharing a cycle, on distinct banks.
+template <int ROWB> __device__ __forceinline__ int swz_k(int r) {
+  return ROWB >= 256 ? (r & 15) : ROWB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+template <int DT, int ROWB> __device__ __forceinline__ int swz_v(int r) {
+  if constexpr (DT == DT_FP8) return swz_k<ROWB>(r);
+  return ROWB >= 256 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+template <int DT, int D, int BN> struct DmaGeo {
+  static constexpr int EB = Traits<DT>::kBytes;
+  static constexpr int ROWB = D * EB;                  // bytes per row
+  static constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
+  static constexpr int TILE = BN * ROWB;               // bytes per tile (one stage)
+  static constexpr int NI = TILE / 1024 / kWaves;      // 1 KiB loads per wavefront per tile
+  static constexpr int LDS_BYTES = 4 * TILE;           // 2 key stages + 2 value stages
+  static_assert(NI >= 1 && TILE % (1024 * kWaves) == 0, "tile must split into 1 KiB loads");
+};
+
+// Issue the loads of one tile (rows k0..k0+BN-1) straight into an LDS stage.
+template <int DT, int D, int BN, bool VALUE>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint8_t* stage, int k0,
+                                         int wave, int lane) {
+  using G = DmaGeo<DT, D, BN>;
+#pragma unroll
+  for (int j = 0; j < G::NI; ++j) {
+    const int blk = wave * G::NI + j;                  // wave-uniform 1 KiB block
+    const int L = blk * 64 + lane;                     // chunk index inside the tile
+    const int row = L / G::CPR, chp = L % G::CPR;
+    const int ch = chp ^ (VALUE ? swz_v<DT, G::ROWB>(row) : swz_k<G::ROWB>(row));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + blk * 1024), 16,
+                                             (k0 + row) * G::ROWB + ch * 16, 0, 0, 0);
+  }
+}
+
+// Per-lane LDS offsets (relative to a stage) used by the operand reads.
+template <int DT, int D, int BN> struct DmaLane {
+  using G = DmaGeo<DT, D, BN>;
+  int kx;      // key operand: row c, this lane's half g, swizzle folded in
+  int vx[2];   // value operand (bf16: two transposed reads; fp8: one)
+  __device__ __forceinline__ DmaLane(int lane) {
+    const int c = lane & 31, g = lane >> 5;
+    if constexpr (DT == DT_BF16) {
+      kx = c * G::ROWB + ((g ^ swz_k<G::ROWB>(c)) << 4);
+      const int q = (lane & 15) >> 2, hi = (lane >> 4) & 1, lo2 = (lane & 3) >> 1;
+      const int qhi = G::ROWB >= 256 ? q : (q >> 1);
+#pragma unroll
+      for (int B = 0; B < 2; ++B)
+        vx[B] = (g * 4 + 8 * B + q) * G::ROWB + (qhi << 6) +
+                ((((hi << 1) | lo2) ^ ((g + 2 * B) & 3)) << 4) + ((lane & 1) << 3);
+    } else {
+      kx = c * G::ROWB + (swz_k<G::ROWB>(c) << 4) + g * 8;
+      const int s = (lane & 15) >> 1, hi = (lane >> 4) & 1;
+      const int keyin = s < 4 ? g * 4 + s : 8 + g * 4 + (s - 4);
+      const int f = swz_k<G::ROWB>(keyin);
+      vx[0] = keyin * G::ROWB + ((hi ^ f) << 4) + ((lane & 1) << 3);
+      vx[1] = 0;
+    }
+  }
+};
+
+// S^T = K Q^T for every 32-key block of a tile held in LDS stage kt.
+template <int DT, int D, int BN>
+__device__ __forceinline__ void qk_dma(f32x16_t (&s)[BN / 32], const uint8_t* kt,
+                                       const typename Traits<DT>::Op (&qop)[D / 16],
+                                       const DmaLane<DT, D, BN>& ln) {
   using TR = Traits<DT>;
-  static constexpr int EB = TR::kBytes;
-  static constexpr int K_STRIDE = D * EB + TR::kKPad;               // bytes per key row
-  static constexpr int K_BYTES = BN * K_STRIDE;
-  static constexpr int V_STRIDE = TR::kVT ? BN * EB + TR::kVPad : D * EB + TR::kVPad;
-  static constexpr int V_ROWS = TR::kVT ? D : BN;
-  static constexpr int V_BYTES = V_ROWS * V_STRIDE;
-  static constexpr int K_OFF_V = (K_BYTES + 15) / 16 * 16;
-  static constexpr int BUF = (K_OFF_V + V_BYTES + 15) / 16 * 16;    // one stage
-  // K tile: 16-byte chunks, row-major, loaded as they are.
-  static constexpr int K_CPR = D * EB / 16;
-  static constexpr int K_CHUNKS = BN * K_CPR;
-  static constexpr int K_PER_THREAD = (K_CHUNKS + kThreads - 1) / kThreads;
-  // V tile, transposed: items of 8 keys x 8 bytes of one key row each.
-  static constexpr int VT_W = 8 / EB;                                // d elements per item row
-  static constexpr int VT_ITEMS = (BN / 8) * (D / (TR::kVT ? VT_W : 1));
-  static constexpr int VT_PER_THREAD = (VT_ITEMS + kThreads - 1) / kThreads;
-  // V tile, natural (fp32): like K.
-  static constexpr int V_CHUNKS = BN * K_CPR;
-  static constexpr int V_PER_THREAD = (V_CHUNKS + kThreads - 1) / kThreads;
-};
-
-// Transposed value rows store the keys of each 16-key group in the order
-// 0-3, 8-11, 4-7, 12-15.  The MFMA B operand of lane half g holds keys
-// {4g..4g+3, 8+4g..8+4g+3} of each 16-key step (the accumulator layout of S^T), so
-// this order lets every lane read its 8 keys with one contiguous load.  A staging
-// item kq covers positions 8kq..8kq+7, i.e. keys kbase+{0..3, 8..11} with
-// kbase = 16*(kq/2) + 4*(kq%2).
-
-template <int DT, int D, int BN>
-struct Staging {
-  using G = Geo<DT, D, BN>;
-  u32x4_t kreg[G::K_PER_THREAD];
-  u32x2_t vreg[Traits<DT>::kVT ? G::VT_PER_THREAD * 8 : 1];
-  u32x4_t vnat[Traits<DT>::kVT ? 1 : G::V_PER_THREAD];
-};
-
-// Issue the global loads of the key/value tile starting at key k0 into registers.
-// Keys at or past Sk are zero-filled.
-template <int DT, int D, int BN>
-__device__ __forceinline__ void load_tile(Staging<DT, D, BN>& st, const uint8_t* Kg,
-                                          const uint8_t* Vg, int k0, int Sk, int tid) {
-  using G = Geo<DT, D, BN>;
-  constexpr int EB = G::EB;
+  using G = DmaGeo<DT, D, BN>;
+  using Op = typename TR::Op;
+  constexpr int KSTEPS = D / 16;
 #pragma unroll
-  for (int r = 0; r < G::K_PER_THREAD; ++r) {
-    const int idx = tid + r * kThreads;
-    u32x4_t val = {0u, 0u, 0u, 0u};
-    if (idx < G::K_CHUNKS) {
-      const int row = idx / G::K_CPR, col = idx % G::K_CPR;
-      const int key = k0 + row;
-      if (key < Sk) val = *reinterpret_cast<const u32x4_t*>(Kg + (size_t(key) * D * EB) + col * 16);
+  for (int b = 0; b < BN / 32; ++b) s[b] = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    // bf16: logical chunk 2ks+g; fp8: chunk ks, half g -- XOR on the chunk field
+    const int x = ln.kx ^ (DT == DT_BF16 ? (ks << 5) : (ks << 4));
+#pragma unroll
+    for (int b = 0; b < BN / 32; ++b) {
+      const Op a = *reinterpret_cast<const Op*>(kt + x + b * 32 * G::ROWB);
+      s[b] = TR::mfma(a, qop[ks], s[b]);
     }
-    st.kreg[r] = val;
   }
-  if constexpr (Traits<DT>::kVT) {
+}
+
+// O^T += V^T P^T for a tile held in LDS stage vt.  Lane (c, g) needs, for output rows
+// d = 32*db + c, the 8 keys {4g..4g+3, 8+4g..8+4g+3} of every 16-key step; the
+// transposed reads deliver exactly those from the row-major value tile.
+template <int DT, int BN> struct PTile;
+template <int DT, int D, int BN>
+__device__ __forceinline__ void pv_dma(f32x16_t (&oacc)[D / 32], const PTile<DT, BN>& pt,
+                                       const uint8_t* vt, const DmaLane<DT, D, BN>& ln) {
+  using TR = Traits<DT>;
+  using G = DmaGeo<DT, D, BN>;
+  using Op = typename TR::Op;
+  constexpr int NDB = D / 32;
 #pragma unroll
-    for (int r = 0; r < G::VT_PER_THREAD; ++r) {
-      const int idx = tid + r * kThreads;
-      const int kq = idx % (BN / 8), dcol = idx / (BN / 8);
-      const int kbase = (kq >> 1) * 16 + (kq & 1) * 4;  // keys kbase+{0..3, 8..11}
+  for (int b = 0; b < BN / 32; ++b) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        u32x2_t val = {0u, 0u};
-        if (idx < G::VT_ITEMS) {
-          const int key = k0 + kbase + (i < 4 ? i : i + 4);
-          if (key < Sk) val = *reinterpret_cast<const u32x2_t*>(Vg + size_t(key) * D * EB + dcol * 8);
+    for (int h = 0; h < 2; ++h) {
+      const Op pb = pt.pk[b][h];
+      const int roff = (b * 32 + h * 16) * G::ROWB;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        Op a;
+        if constexpr (DT == DT_BF16) {
+          const int dx = db << 6;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vt + roff + (ln.vx[0] ^ dx)));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vt + roff + (ln.vx[1] ^ dx)));
+          typedef short i16x8_t __attribute__((ext_vector_type(8)));
+          const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          a = __builtin_bit_cast(Op, both);
+        } else {
+          const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2_t*)(vt + roff + (ln.vx[0] ^ (db << 5))));
+          a = __builtin_bit_cast(Op, v);
         }
-        st.vreg[r * 8 + i] = val;
+        oacc[db] = TR::mfma(a, pb, oacc[db]);
       }
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < G::V_PER_THREAD; ++r) {
-      const int idx = tid + r * kThreads;
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (idx < G::V_CHUNKS) {
-        const int row = idx / G::K_CPR, col = idx % G::K_CPR;
-        const int key = k0 + row;
-        if (key < Sk) val = *reinterpret_cast<const u32x4_t*>(Vg + size_t(key) * D * EB + col * 16);
-      }
-      st.vnat[r] = val;
     }
   }
 }
 
-// Write 16 bytes to LDS at a byte offset that is a multiple of ALIGN.
-template <int ALIGN>
-__device__ __forceinline__ void lds_store16(uint8_t* p, u32x4_t v) {
-  if constexpr (ALIGN % 16 == 0) {
-    *reinterpret_cast<u32x4_t*>(p) = v;
-  } else if constexpr (ALIGN % 8 == 0) {
-    reinterpret_cast<u32x2_t*>(p)[0] = u32x2_t{v[0], v[1]};
-    reinterpret_cast<u32x2_t*>(p)[1] = u32x2_t{v[2], v[3]};
-  } else {
-    uint32_t* q = reinterpret_cast<uint32_t*>(p);
-    q[0] = v[0]; q[1] = v[1]; q[2] = v[2]; q[3] = v[3];
-  }
-}
+// ================================================================== register-staged tiles (fp32)
+// fp32 tiles go through registers into padded LDS rows: keys row-major, values
+// row-major (the fp32 MFMA takes one element per lane, so no transpose is needed).
+template <int D, int BN> struct StGeo {
+  static constexpr int EB = 4;
+  static constexpr int K_STRIDE = D * EB + 4;                        // odd dword stride
+  static constexpr int V_STRIDE = D * EB + 16;
+  static constexpr int K_BYTES = (BN * K_STRIDE + 15) / 16 * 16;
+  static constexpr int V_BYTES = (BN * V_STRIDE + 15) / 16 * 16;
+  static constexpr int LDS_BYTES = 2 * (K_BYTES + V_BYTES);
+  static constexpr int CPR = D * EB / 16;
+  static constexpr int CHUNKS = BN * CPR;
+  static constexpr int PER_THREAD = (CHUNKS + kThreads - 1) / kThreads;
+};
 
-// Move the staged tile from registers into one LDS stage.
-template <int DT, int D, int BN>
-__device__ __forceinline__ void store_tile(const Staging<DT, D, BN>& st, uint8_t* buf, int tid) {
-  using G = Geo<DT, D, BN>;
-  uint8_t* kb = buf;
-  uint8_t* vb = buf + G::K_OFF_V;
+template <int D, int BN> struct StRegs {
+  u32x4_t r[StGeo<D, BN>::PER_THREAD];
+};
+
+template <int D, int BN>
+__device__ __forceinline__ void st_load(StRegs<D, BN>& st, __amdgpu_buffer_rsrc_t rs, int k0, int tid) {
+  using G = StGeo<D, BN>;
 #pragma unroll
-  for (int r = 0; r < G::K_PER_THREAD; ++r) {
+  for (int r = 0; r < G::PER_THREAD; ++r) {
     const int idx = tid + r * kThreads;
-    if (idx < G::K_CHUNKS) {
-      const int row = idx / G::K_CPR, col = idx % G::K_CPR;
-      lds_store16<(G::K_STRIDE % 16 == 0) ? 16 : (G::K_STRIDE % 8 == 0 ? 8 : 4)>(
-          kb + row * G::K_STRIDE + col * 16, st.kreg[r]);
+    if (G::CHUNKS % kThreads == 0 || idx < G::CHUNKS) {
+      const int row = idx / G::CPR, col = idx % G::CPR;
+      st.r[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, (k0 + row) * (D * G::EB) + col * 16, 0, 0);
     }
   }
-  if constexpr (Traits<DT>::kVT) {
+}
+
+template <int D, int BN, int STRIDE>
+__device__ __forceinline__ void st_store(const StRegs<D, BN>& st, uint8_t* dst, int tid) {
+  using G = StGeo<D, BN>;
 #pragma unroll
-    for (int r = 0; r < G::VT_PER_THREAD; ++r) {
-      const int idx = tid + r * kThreads;
-      if (idx >= G::VT_ITEMS) continue;
-      const int kq = idx % (BN / 8), dcol = idx / (BN / 8);
-      const u32x2_t* in = &st.vreg[r * 8];
-      if constexpr (DT == DT_BF16) {
-        // in[i] holds d = 4*dcol + {0,1} (word 0) and {2,3} (word 1) of key i.
-        // Output row e (d = 4*dcol + e) is 8 keys x 2 bytes = 4 words.
+  for (int r = 0; r < G::PER_THREAD; ++r) {
+    const int idx = tid + r * kThreads;
+    if (G::CHUNKS % kThreads == 0 || idx < G::CHUNKS) {
+      const int row = idx / G::CPR, col = idx % G::CPR;
+      uint32_t* q = reinterpret_cast<uint32_t*>(dst + row * STRIDE + col * 16);
+      if constexpr (STRIDE % 16 == 0) {
+        *reinterpret_cast<u32x4_t*>(q) = st.r[r];
+      } else {
+        q[0] = st.r[r][0]; q[1] = st.r[r][1]; q[2] = st.r[r][2]; q[3] = st.r[r][3];
+      }
+    }
+  }
+}
+
+template <int D, int BN>
+__device__ __forceinline__ void qk_st(f32x16_t (&s)[BN / 32], const uint8_t* kb,
+                                      const float (&qop)[D / 2], int c, int g) {
+  using G = StGeo<D, BN>;
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b) {
+    s[b] = f32x16_t{};
+    const uint8_t* krow = kb + (b * 32 + c) * G::K_STRIDE + g * 4;
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks)
+      s[b] = Traits<DT_F32>::mfma(*reinterpret_cast<const float*>(krow + ks * 8), qop[ks], s[b]);
+  }
+}
+
+template <int D, int BN>
+__device__ __forceinline__ void pv_st(f32x16_t (&oacc)[D / 32], const f32x16_t (&s)[BN / 32],
+                                      const uint8_t* vb, int c, int g) {
+  using G = StGeo<D, BN>;
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+      const int key = b * 32 + (tt >> 2) * 8 + g * 4 + (tt & 3);
+      const uint8_t* vrow = vb + key * G::V_STRIDE + c * 4;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        oacc[db] = Traits<DT_F32>::mfma(*reinterpret_cast<const float*>(vrow + db * 128),
+                                        s[b][tt], oacc[db]);
+    }
+}
+
+// ================================================================== softmax
+// Keys past the chunk / sequence end, and keys above the causal diagonal, become -inf.
+template <int BN>
+__device__ __forceinline__ void mask_tile(f32x16_t (&s)[BN / 32], int k0, int kend, int row,
+                                          int off, bool causal, int g) {
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = k0 + b * 32 + (j >> 2) * 8 + g * 4 + (j & 3);
+      const bool vis = key < kend && (!causal || key <= row + off);
+      if (!vis) s[b][j] = -__builtin_inff();
+    }
+}
+
+// Probabilities of a tile in the form the value MFMA consumes: for bf16 and fp8 the
+// packed B operands of each 16-key step (pk[b][h] holds elements 8h..8h+7 of score
+// block b); for fp32 the scores themselves, overwritten in place.
+template <int DT, int BN> struct PTile {
+  typename Traits<DT>::Op pk[BN / 32][2];
+};
+template <int BN> struct PTile<DT_F32, BN> {};
+
+// Online-softmax step for one tile: update the reference maximum (lazily), rescale the
+// accumulator when it moves, and produce the unnormalised probabilities
+// exp2(s * scale_log2 - m).  Two row sums are kept: l_run of the probabilities as
+// computed (it gives the log-sum-exp), and c_run of exactly the rounded values that
+// enter the value MFMA (it normalises O).  With c_run, numerator and denominator of O
+// agree, so a row dominated by one key returns that key's value up to accumulation
+// error instead of off by the rounding of its probability.
+template <int DT, int BN, int NDB>
+__device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], PTile<DT, BN>& pt,
+                                             f32x16_t (&oacc)[NDB], float& m_run, float& l_run,
+                                             float& c_run, float sl2) {
+  using TR = Traits<DT>;
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, s[b][j]);
+  mx = pair_max(mx);
+  const float mt = mx * sl2;
+  if (__builtin_amdgcn_ballot_w64(mt > m_run + TR::kTau)) {
+    const float m_new = __builtin_fmaxf(m_run, mt);
+    const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+    c_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
+    m_run = m_new;
+  }
+  const float ms = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+  float ls = 0.0f;
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      s[b][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][j], sl2, -ms));
+      ls += s[b][j];
+    }
+  l_run += ls;
+  if constexpr (DT == DT_BF16) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float cs = 0.0f;
+#pragma unroll
+    for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x8_t x = {s[b][8 * h + 0], s[b][8 * h + 1], s[b][8 * h + 2], s[b][8 * h + 3],
+                     s[b][8 * h + 4], s[b][8 * h + 5], s[b][8 * h + 6], s[b][8 * h + 7]};
+        const bf16x8_t v = __builtin_convertvector(x, bf16x8_t);
+        pt.pk[b][h] = v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int w = e >> 1;
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          u32x4_t o;
-          o[0] = __builtin_amdgcn_perm(in[1][w], in[0][w], sel);
-          o[1] = __builtin_amdgcn_perm(in[3][w], in[2][w], sel);
-          o[2] = __builtin_amdgcn_perm(in[5][w], in[4][w], sel);
-          o[3] = __builtin_amdgcn_perm(in[7][w], in[6][w], sel);
-          *reinterpret_cast<u32x4_t*>(vb + (dcol * 4 + e) * G::V_STRIDE + kq * 16) = o;
-        }
-      } else {
-        // fp8: in[i] holds d = 8*dcol + 0..3 (word 0) and 4..7 (word 1) of key i.
-        // Output row e is 8 keys x 1 byte = 2 words.
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 2, b = e & 3;
-          const uint32_t s2 = uint32_t(b) | (uint32_t(b + 4) << 8);  // byte b of lo, byte b of hi
-          const uint32_t t01 = __builtin_amdgcn_perm(in[1][w], in[0][w], s2);
-          const uint32_t t23 = __builtin_amdgcn_perm(in[3][w], in[2][w], s2);
-          const uint32_t t45 = __builtin_amdgcn_perm(in[5][w], in[4][w], s2);
-          const uint32_t t67 = __builtin_amdgcn_perm(in[7][w], in[6][w], s2);
-          u32x2_t o;
-          o[0] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-          o[1] = __builtin_amdgcn_perm(t67, t45, 0x05040100u);
-          *reinterpret_cast<u32x2_t*>(vb + (dcol * 8 + e) * G::V_STRIDE + kq * 8) = o;
+          const bf16x2_t two = {v[2 * e], v[2 * e + 1]};
+          cs = __builtin_amdgcn_fdot2_f32_bf16(two, ones, cs, false);
         }
       }
-    }
+    c_run += cs;
+  } else if constexpr (DT == DT_FP8) {
+    const float k = TR::kPScale;
+    float cs = 0.0f;
+#pragma unroll
+    for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int w[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int e = 8 * h + 4 * q;
+          int v = __builtin_amdgcn_cvt_pk_fp8_f32(s[b][e + 0] * k, s[b][e + 1] * k, 0, false);
+          v = __builtin_amdgcn_cvt_pk_fp8_f32(s[b][e + 2] * k, s[b][e + 3] * k, v, true);
+          w[q] = v;
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
+          cs += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+        }
+        pt.pk[b][h] = (long)(((unsigned long)(uint32_t)w[1] << 32) | (uint32_t)w[0]);
+      }
+    c_run += cs * (1.0f / k);
   } else {
-#pragma unroll
-    for (int r = 0; r < G::V_PER_THREAD; ++r) {
-      const int idx = tid + r * kThreads;
-      if (idx < G::V_CHUNKS) {
-        const int row = idx / G::K_CPR, col = idx % G::K_CPR;
-        lds_store16<(G::V_STRIDE % 16 == 0) ? 16 : 4>(vb + row * G::V_STRIDE + col * 16, st.vnat[r]);
-      }
-    }
+    c_run += ls;
   }
-}
-
-// Probabilities of one 16-key MFMA step (elements 8h..8h+7 of a score block) as the
-// B operand of the value product.
-template <int DT>
-__device__ __forceinline__ typename Traits<DT>::Op pack_p(const f32x16_t& s, int h);
-
-template <>
-__device__ __forceinline__ bf16x8_t pack_p<DT_BF16>(const f32x16_t& s, int h) {
-  f32x8_t x = {s[8 * h + 0], s[8 * h + 1], s[8 * h + 2], s[8 * h + 3],
-               s[8 * h + 4], s[8 * h + 5], s[8 * h + 6], s[8 * h + 7]};
-  return __builtin_convertvector(x, bf16x8_t);
-}
-
-template <>
-__device__ __forceinline__ long pack_p<DT_FP8>(const f32x16_t& s, int h) {
-  const float k = Traits<DT_FP8>::kPScale;
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[8 * h + 0] * k, s[8 * h + 1] * k, 0, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[8 * h + 2] * k, s[8 * h + 3] * k, lo, true);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[8 * h + 4] * k, s[8 * h + 5] * k, 0, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[8 * h + 6] * k, s[8 * h + 7] * k, hi, true);
-  return (long)(((unsigned long)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
 constexpr int waves_per_eu(int dt, int d) { return (d >= 256 || dt == DT_F32) ? 1 : 2; }
 
-// ------------------------------------------------------------------ forward kernel
+// ================================================================== tile pipeline
+// Uniform interface over the two ways tiles reach LDS.  issue_*: start the loads of a
+// tile (direct-to-LDS loads already target the stage); commit_*: registers -> LDS for
+// the staged variant, nothing for the direct one.
+template <int DT, int D, int BN, bool DMA = Traits<DT>::kDMA> struct Pipe;
+
+template <int DT, int D, int BN> struct Pipe<DT, D, BN, true> {
+  using G = DmaGeo<DT, D, BN>;
+  using Op = typename Traits<DT>::Op;
+  static constexpr int STAGE_K = G::TILE, STAGE_V = G::TILE;
+  static constexpr int NSTAGE = 4;
+  static constexpr int KSTEPS = D / 16;
+  // Wait until at most N iterations' worth of tile loads are still in flight.
+  template <int N> __device__ __forceinline__ static void wait_loads() {
+    constexpr int n = N * 2 * G::NI;  // key + value loads per thread per iteration
+    static_assert(n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+  }
+  DmaLane<DT, D, BN> ln;
+  int wave, lane;
+  __device__ __forceinline__ Pipe(int w, int l) : ln(l), wave(w), lane(l) {}
+  __device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t rs, int k0, uint8_t* dst) {
+    dma_tile<DT, D, BN, false>(rs, dst, k0, wave, lane);
+  }
+  __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rs, int k0, uint8_t* dst) {
+    dma_tile<DT, D, BN, true>(rs, dst, k0, wave, lane);
+  }
+  __device__ __forceinline__ void commit_k(uint8_t*, int) {}
+  __device__ __forceinline__ void commit_v(uint8_t*, int) {}
+  __device__ __forceinline__ void qk(f32x16_t (&s)[BN / 32], const uint8_t* kt, const Op (&qop)[KSTEPS]) {
+    qk_dma<DT, D, BN>(s, kt, qop, ln);
+  }
+  __device__ __forceinline__ void pv(f32x16_t (&oacc)[D / 32], const f32x16_t (&)[BN / 32],
+                                     const PTile<DT, BN>& pt, const uint8_t* vt) {
+    pv_dma<DT, D, BN>(oacc, pt, vt, ln);
+  }
+};
+
+template <int DT, int D, int BN> struct Pipe<DT, D, BN, false> {
+  using G = StGeo<D, BN>;
+  using Op = float;
+  static constexpr int STAGE_K = G::K_BYTES, STAGE_V = G::V_BYTES;
+  static constexpr int NSTAGE = 2;
+  static constexpr int KSTEPS = D / 2;
+  template <int N> __device__ __forceinline__ static void wait_loads() { wait_vmem(); }
+  StRegs<D, BN> rk, rv;
+  int c, g;
+  __device__ __forceinline__ Pipe(int w, int l) : c(l & 31), g(l >> 5) { (void)w; }
+  __device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t rs, int k0, uint8_t*) {
+    st_load<D, BN>(rk, rs, k0, threadIdx.x);
+  }
+  __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rs, int k0, uint8_t*) {
+    st_load<D, BN>(rv, rs, k0, threadIdx.x);
+  }
+  __device__ __forceinline__ void commit_k(uint8_t* dst, int tid) { st_store<D, BN, G::K_STRIDE>(rk, dst, tid); }
+  __device__ __forceinline__ void commit_v(uint8_t* dst, int tid) { st_store<D, BN, G::V_STRIDE>(rv, dst, tid); }
+  __device__ __forceinline__ void qk(f32x16_t (&s)[BN / 32], const uint8_t* kt, const float (&qop)[KSTEPS]) {
+    qk_st<D, BN>(s, kt, qop, c, g);
+  }
+  __device__ __forceinline__ void pv(f32x16_t (&oacc)[D / 32], const f32x16_t (&s)[BN / 32],
+                                     const PTile<DT_F32, BN>&, const uint8_t* vt) {
+    pv_st<D, BN>(oacc, s, vt, c, g);
+  }
+};
+
+// ================================================================== forward kernel
 template <int DT, int D, int BN, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(waves_per_eu(DT, D), waves_per_eu(DT, D))))
 void attn_fwd_kernel(FwdArgs p) {
   using TR = Traits<DT>;
-  using G = Geo<DT, D, BN>;
+  using P = Pipe<DT, D, BN>;
   using Op = typename TR::Op;
   constexpr int EB = TR::kBytes;
   constexpr int KSTEPS = D / TR::kKS;  // MFMAs over d per 32-key block of S^T
   constexpr int NKB = BN / 32;         // 32-key blocks per tile
   constexpr int NDB = D / 32;          // 32-row blocks of O^T
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * G::BUF];
-
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, g = lane >> 5;
 
   // ---- which (batch*head, query tile, split) this workgroup owns.  The linear index
@@ -338,6 +550,7 @@ void attn_fwd_kernel(FwdArgs p) {
   const int r0 = q0 + wave * kRowsPerWave;    // first query row of this wavefront
   const int row = r0 + c;                     // query row of this lane
   const int off = p.Sk - p.Sq;                // causal: key j visible to row i iff j <= i + off
+  const int wave_last = min(r0 + kRowsPerWave - 1, p.Sq - 1);
 
   int kbeg = 0, kend = p.Sk;
   if (SPLIT) {
@@ -355,17 +568,26 @@ void attn_fwd_kernel(FwdArgs p) {
 
   const size_t q_base = size_t(bh) * p.Sq * D;
   const size_t kv_base = size_t(bh) * p.Sk * D;
-  const uint8_t* Qg = reinterpret_cast<const uint8_t*>(p.q) + q_base * EB;
-  const uint8_t* Kg = reinterpret_cast<const uint8_t*>(p.k) + kv_base * EB;
-  const uint8_t* Vg = reinterpret_cast<const uint8_t*>(p.v) + kv_base * EB;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint8_t*>(p.q) + q_base * EB,
+                                              uint32_t(p.Sq) * D * EB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + kv_base * EB,
+                                              uint32_t(p.Sk) * D * EB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + kv_base * EB,
+                                              uint32_t(p.Sk) * D * EB);
 
-  // ---- Q operands for the whole sweep, in registers (B operand of S^T = K Q^T).
+  // ---- Q operands for the whole sweep, in registers (B operand of S^T = K Q^T);
+  // rows past Sq read as zeros.
   Op qop[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    qop[ks] = (row < p.Sq)
-                  ? TR::load(Qg + (size_t(row) * D + ks * TR::kKS + g * TR::kKPL) * EB)
-                  : TR::zero();
+    const int boff = (row * D + ks * TR::kKS + g * TR::kKPL) * EB;
+    if constexpr (DT == DT_BF16) {
+      qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b128(rq, boff, 0, 0));
+    } else if constexpr (DT == DT_FP8) {
+      qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b64(rq, boff, 0, 0));
+    } else {
+      qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b32(rq, boff, 0, 0));
+    }
   }
 
   f32x16_t oacc[NDB];
@@ -373,135 +595,144 @@ void attn_fwd_kernel(FwdArgs p) {
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16_t{};
   float m_run = -__builtin_inff();  // reference maximum, log2 units (same in lanes c, c+32)
   float l_run = 0.0f;               // this lane's share of the row sum
+  float c_run = 0.0f;               // same, of the probabilities as rounded for the MFMA
   const float sl2 = p.scale_log2;
 
-  Staging<DT, D, BN> st;
+  // A tile starting at key k0 has work for this wavefront unless every row of the
+  // wavefront is past Sq or (causal) every key of the tile is above its diagonal.
+  auto active = [&](int k0) __attribute__((always_inline)) { return r0 < p.Sq && (!p.causal || k0 <= wave_last + off); };
+  auto needs_mask = [&](int k0) __attribute__((always_inline)) { return (k0 + BN > kend) || (p.causal && (k0 + BN - 1 > r0 + off)); };
+
+  P pipe(wave, lane);
+  // NS-stage rings for key and value tiles.  Tile j lives in stage j % NS of each
+  // ring.  The sweep is unrolled by NS, so every LDS access names a compile-time
+  // stage and the direct-to-LDS loads still in flight provably do not alias the
+  // stages being read (no wait is needed before the operand reads).
+  constexpr int NS = P::NSTAGE;
+  static_assert(NS == 2 || NS == 4, "stage count");
+  // one named array per stage: the wait insertion only tells distinct objects apart
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[P::STAGE_K], ks1[P::STAGE_K];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks2[NS > 2 ? P::STAGE_K : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks3[NS > 2 ? P::STAGE_K : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[P::STAGE_V], vs1[P::STAGE_V];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs2[NS > 2 ? P::STAGE_V : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs3[NS > 2 ? P::STAGE_V : 1];
+  auto kst = [&](int j) __attribute__((always_inline)) -> uint8_t* {
+    return (j & 3) == 0 ? ks0 : (j & 3) == 1 ? ks1 : (j & 3) == 2 ? ks2 : ks3;
+  };
+  auto vst = [&](int j) __attribute__((always_inline)) -> uint8_t* {
+    return (j & 3) == 0 ? vs0 : (j & 3) == 1 ? vs1 : (j & 3) == 2 ? vs2 : vs3;
+  };
+
+  // ---- prologue: key tiles 0..NS-1 and value tiles 0..NS-2 in flight, then S^T of
+  // tile 0 once key tile 0 has landed.  Loads are issued unconditionally (tiles past
+  // the end read as zeros and are never used) so that every iteration has the same
+  // number of loads in flight and the partial waits below stay exact.
   if (ntiles > 0) {
-    load_tile<DT, D, BN>(st, Kg, Vg, kbeg, p.Sk, tid);
-    store_tile<DT, D, BN>(st, smem, tid);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = kbeg + t * BN;
-    if (t + 1 < ntiles) load_tile<DT, D, BN>(st, Kg, Vg, k0 + BN, p.Sk, tid);
-    const uint8_t* kb = smem + (t & 1) * G::BUF;
-    const uint8_t* vb = kb + G::K_OFF_V;
-
-    bool active = r0 < p.Sq;
-    if (p.causal) active = active && (k0 <= min(r0 + kRowsPerWave - 1, p.Sq - 1) + off);
-    if (active) {
-      // ---- S^T = K Q^T for the tile's 32-key blocks
-      f32x16_t s[NKB];
 #pragma unroll
-      for (int b = 0; b < NKB; ++b) {
-        s[b] = f32x16_t{};
-        const uint8_t* krow = kb + (b * 32 + c) * G::K_STRIDE + g * TR::kKPL * EB;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-          s[b] = TR::mfma(TR::load(krow + ks * TR::kKS * EB), qop[ks], s[b]);
-      }
-      // ---- masks: keys past the chunk / sequence end, and the causal diagonal
-      const bool need_mask = (k0 + BN > kend) || (p.causal && (k0 + BN - 1 > r0 + off));
-      if (need_mask) {
-#pragma unroll
-        for (int b = 0; b < NKB; ++b)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + b * 32 + (j >> 2) * 8 + g * 4 + (j & 3);
-            const bool vis = key < kend && (!p.causal || key <= row + off);
-            if (!vis) s[b][j] = -__builtin_inff();
-          }
-      }
-      // ---- online softmax (log2 units)
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int b = 0; b < NKB; ++b)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = mx > s[b][j] ? mx : s[b][j];
-      mx = pair_max(mx);
-      const float mt = mx * sl2;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + TR::kTau)) {
-        const float m_new = m_run > mt ? m_run : mt;
-        const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
-        m_run = m_new;
-      }
-      const float ms = (m_run == -__builtin_inff()) ? 0.0f : m_run;
-      float ls = 0.0f;
-#pragma unroll
-      for (int b = 0; b < NKB; ++b)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][j], sl2, -ms));
-          s[b][j] = e;
-          ls += e;
-        }
-      l_run += ls;
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int b = 0; b < NKB; ++b) {
-        if constexpr (TR::kVT) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const Op pb = pack_p<DT>(s[b], h);
-            const uint8_t* vrow = vb + c * G::V_STRIDE + (b * 32 + h * 16 + g * 8) * EB;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-              oacc[db] = TR::mfma(TR::load(vrow + db * 32 * G::V_STRIDE), pb, oacc[db]);
-          }
-        } else {
-#pragma unroll
-          for (int tt = 0; tt < 16; ++tt) {
-            const int key = b * 32 + (tt >> 2) * 8 + g * 4 + (tt & 3);
-            const uint8_t* vrow = vb + key * G::V_STRIDE + c * EB;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-              oacc[db] = TR::mfma(TR::load(vrow + db * 32 * EB), s[b][tt], oacc[db]);
-          }
-        }
+    for (int j = 0; j < NS; ++j) {
+      pipe.issue_k(rk, kbeg + j * BN, kst(j));
+      pipe.commit_k(kst(j), tid);
+      if (j < NS - 1) {
+        pipe.issue_v(rv, kbeg + j * BN, vst(j));
+        pipe.commit_v(vst(j), tid);
       }
     }
-    if (t + 1 < ntiles) store_tile<DT, D, BN>(st, smem + ((t + 1) & 1) * G::BUF, tid);
-    __syncthreads();
   }
+  wait_vmem();
+  block_sync();
+  f32x16_t sa[NKB], sb[NKB];
+  bool act_cur = ntiles > 0 && active(kbeg);
+  if (act_cur) pipe.qk(sa, kst(0), qop);
+  block_sync();
+
+  // ---- key sweep.  Iteration t: S^T of tile t+1 is computed while tile t's softmax
+  // runs; then O^T += V^T P^T with tile t's values.  Key tile t+NS and value tile
+  // t+NS-1 are requested into the stages that iteration t-1 finished reading; at the
+  // end of the iteration only the loads that iteration t+1 needs are waited for.
+  auto step = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
+                  f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB]) __attribute__((always_inline)) {
+    const int k0 = kbeg + t * BN;
+    const bool has1 = t + 1 < ntiles;
+    pipe.issue_k(rk, k0 + NS * BN, kdst);
+    pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
+    const bool act_next = has1 && active(k0 + BN);
+    if (act_cur && act_next && !needs_mask(k0)) {
+      // steady state: one basic block, so the scheduler can interleave the score
+      // MFMAs of the next tile with this tile's exponentials
+      PTile<DT, BN> pt;
+      pipe.qk(s_next, kb, qop);
+      softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
+      pipe.pv(oacc, s_cur, pt, vb);
+    } else {
+      if (act_next) pipe.qk(s_next, kb, qop);
+      if (act_cur) {
+        if (needs_mask(k0)) mask_tile<BN>(s_cur, k0, kend, row, off, p.causal, g);
+        PTile<DT, BN> pt;
+        softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
+        pipe.pv(oacc, s_cur, pt, vb);
+      }
+    }
+    pipe.commit_k(kdst, tid);
+    pipe.commit_v(vdst, tid);
+    // Loads complete in order and every iteration issues the same number, so leaving
+    // the newest (NS-2) iterations' loads in flight guarantees that key tile t+2 and
+    // value tile t+1 have landed.
+    P::template wait_loads<NS - 2>();
+    block_sync();
+    act_cur = act_next;
+  };
+  // The sweep is unrolled by NS by hand, so that stage indices are constants.
+  auto step_j = [&](auto jc, int t) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    if (t + j < ntiles) {
+      if constexpr (j % 2 == 0)
+        step(t + j, kst(j), vst((j + NS - 1) % NS), kst((j + 1) % NS), vst(j), sa, sb);
+      else
+        step(t + j, kst(j), vst((j + NS - 1) % NS), kst((j + 1) % NS), vst(j), sb, sa);
+    }
+  };
+  for (int t = 0; t < ntiles; t += NS) {
+    step_j(std::integral_constant<int, 0>{}, t);
+    step_j(std::integral_constant<int, 1>{}, t);
+    if constexpr (NS > 2) {
+      step_j(std::integral_constant<int, 2>{}, t);
+      step_j(std::integral_constant<int, 3>{}, t);
+    }
+  }
+  wait_vmem();
 
   // ---- write-back: deferred normalisation
   const float l_tot = pair_sum(l_run);
+  const float c_tot = pair_sum(c_run);
   if (row >= p.Sq) return;
   const size_t ridx = size_t(bh) * p.Sq + row;
+  float* out;
+  float sc;
   if constexpr (!SPLIT) {
-    const float inv = l_tot > 0.0f ? p.v_scale / (TR::kPScale * l_tot) : 0.0f;
-    float* orow = p.o + ridx * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        f32x4_t v4 = {oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2],
-                      oacc[db][4 * jj + 3]};
-        *reinterpret_cast<f32x4_t*>(orow + db * 32 + jj * 8 + g * 4) = v4 * inv;
-      }
+    out = p.o + ridx * D;
+    sc = c_tot > 0.0f ? p.v_scale / (TR::kPScale * c_tot) : 0.0f;
     if (g == 0)
       p.lse[ridx] = l_tot > 0.0f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
   } else {
+    // u is stored as (l / c) * sum(rounded p * v): u / l is then the chunk's consistent
+    // weighted average, while u still equals sum(exp(s - m) v) up to rounding.
     const size_t sidx = size_t(split) * size_t(BH) * p.Sq + ridx;
-    const float us = p.v_scale / TR::kPScale;
-    float* urow = p.ws_u + sidx * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        f32x4_t v4 = {oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2],
-                      oacc[db][4 * jj + 3]};
-        *reinterpret_cast<f32x4_t*>(urow + db * 32 + jj * 8 + g * 4) = v4 * us;
-      }
+    out = p.ws_u + sidx * D;
+    sc = c_tot > 0.0f ? p.v_scale * l_tot / (TR::kPScale * c_tot) : 0.0f;
     if (g == 0) {
       p.ws_m[sidx] = l_tot > 0.0f ? m_run * kLn2 : -__builtin_inff();
       p.ws_l[sidx] = l_tot;
     }
   }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      f32x4_t v4 = {oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2],
+                    oacc[db][4 * jj + 3]};
+      *reinterpret_cast<f32x4_t*>(out + db * 32 + jj * 8 + g * 4) = v4 * sc;
+    }
 }
 
 // ------------------------------------------------------------------ merge kernel
