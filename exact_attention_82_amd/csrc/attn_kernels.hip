@@ -650,29 +650,7 @@ void attn_fwd_kernel(FwdArgs p) {
   // runs; then O^T += V^T P^T with tile t's values.  Key tile t+NS and value tile
   // t+NS-1 are requested into the stages that iteration t-1 finished reading; at the
   // end of the iteration only the loads that iteration t+1 needs are waited for.
-  auto step = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
-                  f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB]) __attribute__((always_inline)) {
-    const int k0 = kbeg + t * BN;
-    const bool has1 = t + 1 < ntiles;
-    pipe.issue_k(rk, k0 + NS * BN, kdst);
-    pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
-    const bool act_next = has1 && active(k0 + BN);
-    if (act_cur && act_next && !needs_mask(k0)) {
-      // steady state: one basic block, so the scheduler can interleave the score
-      // MFMAs of the next tile with this tile's exponentials
-      PTile<DT, BN> pt;
-      pipe.qk(s_next, kb, qop);
-      softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
-      pipe.pv(oacc, s_cur, pt, vb);
-    } else {
-      if (act_next) pipe.qk(s_next, kb, qop);
-      if (act_cur) {
-        if (needs_mask(k0)) mask_tile<BN>(s_cur, k0, kend, row, off, p.causal, g);
-        PTile<DT, BN> pt;
-        softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
-        pipe.pv(oacc, s_cur, pt, vb);
-      }
-    }
+  auto finish = [&](uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
     pipe.commit_k(kdst, tid);
     pipe.commit_v(vdst, tid);
     // Loads complete in order and every iteration issues the same number, so leaving
@@ -680,26 +658,76 @@ void attn_fwd_kernel(FwdArgs p) {
     // value tile t+1 have landed.
     P::template wait_loads<NS - 2>();
     block_sync();
-    act_cur = act_next;
   };
-  // The sweep is unrolled by NS by hand, so that stage indices are constants.
-  auto step_j = [&](auto jc, int t) __attribute__((always_inline)) {
-    constexpr int j = decltype(jc)::value;
-    if (t + j < ntiles) {
-      if constexpr (j % 2 == 0)
-        step(t + j, kst(j), vst((j + NS - 1) % NS), kst((j + 1) % NS), vst(j), sa, sb);
-      else
-        step(t + j, kst(j), vst((j + NS - 1) % NS), kst((j + 1) % NS), vst(j), sb, sa);
-    }
+  // Main part: tiles with a successor that are visible to every row of the workgroup
+  // (no mask, every wavefront active).  One straight-line block per tile.
+  auto step_full = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
+                       f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB]) __attribute__((always_inline)) {
+    const int k0 = kbeg + t * BN;
+    pipe.issue_k(rk, k0 + NS * BN, kdst);
+    pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
+    PTile<DT, BN> pt;
+    pipe.qk(s_next, kb, qop);
+    softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
+    pipe.pv(oacc, s_cur, pt, vb);
+    finish(kdst, vdst);
   };
-  for (int t = 0; t < ntiles; t += NS) {
-    step_j(std::integral_constant<int, 0>{}, t);
-    step_j(std::integral_constant<int, 1>{}, t);
-    if constexpr (NS > 2) {
-      step_j(std::integral_constant<int, 2>{}, t);
-      step_j(std::integral_constant<int, 3>{}, t);
+  // Remaining tiles: the causal diagonal band, the sequence / chunk tail, the last tile.
+  auto step_edge = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
+                       f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB]) __attribute__((always_inline)) {
+    const int k0 = kbeg + t * BN;
+    const bool act_cur = active(k0);
+    const bool act_next = t + 1 < ntiles && active(k0 + BN);
+    pipe.issue_k(rk, k0 + NS * BN, kdst);
+    pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
+    if (act_next) pipe.qk(s_next, kb, qop);
+    if (act_cur) {
+      if (needs_mask(k0)) mask_tile<BN>(s_cur, k0, kend, row, off, p.causal, g);
+      PTile<DT, BN> pt;
+      softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
+      pipe.pv(oacc, s_cur, pt, vb);
     }
+    finish(kdst, vdst);
+  };
+  // Tiles [0, nfull) are full: start below every row's diagonal (causal) and end
+  // before kend; nfull is rounded down to a multiple of NS so that both loops start on
+  // stage 0 and the sweep stays unrolled by NS with constant stage indices.
+  int nfull = ntiles - 1;
+  {
+    const int lim_end = (kend - kbeg) / BN;  // tiles ending at or before kend
+    nfull = min(nfull, lim_end);
+    if (p.causal) {
+      // tile t is fully visible to the workgroup's first row iff k0 + BN - 1 <= q0 + off
+      const int d = q0 + off - kbeg - (BN - 1);
+      nfull = min(nfull, d < 0 ? 0 : d / BN + 1);
+    }
+    if (r0 >= p.Sq) nfull = 0;  // wavefronts with no row take the guarded path
+    // Both loops pass one barrier per tile, so wavefronts may split at different tiles.
+    nfull = nfull < 0 ? 0 : (nfull / NS) * NS;
   }
+  auto run = [&](auto full_c, int t0, int t1) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_c)::value;
+    for (int t = t0; t < t1; t += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        if (t + j < t1) {
+          uint8_t* kd = kst(j);
+          uint8_t* vd = vst((j + NS - 1) % NS);
+          const uint8_t* kb = kst((j + 1) % NS);
+          const uint8_t* vb = vst(j);
+          if (j % 2 == 0) {
+            if constexpr (FULL) step_full(t + j, kd, vd, kb, vb, sa, sb);
+            else step_edge(t + j, kd, vd, kb, vb, sa, sb);
+          } else {
+            if constexpr (FULL) step_full(t + j, kd, vd, kb, vb, sb, sa);
+            else step_edge(t + j, kd, vd, kb, vb, sb, sa);
+          }
+        }
+      }
+    }
+  };
+  run(std::true_type{}, 0, nfull);
+  run(std::false_type{}, nfull, ntiles);
   wait_vmem();
 
   // ---- write-back: deferred normalisation
