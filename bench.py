@@ -202,7 +202,7 @@ def main():
             "workload": f"{args.workload}: B={B}, H={H}, Sq=Sk={S}, d={d}, bf16 N(0,1) inputs, "
                         "fp32 O + lse; one step = non-causal + causal forward",
             "B": B, "H": H, "Sq": S, "Sk": S, "d": d, "masks": ["non-causal", "causal"],
-            "kernel": ea.attn_kernel_name(d, ea.ATTN_BF16),
+            "kernels": {m: ea.attn_kernel_name(B, H, S, d, c, ea.ATTN_BF16) for m, c in (("non_causal", 0), ("causal", 1))},
         },
         "modes": {
             ("causal" if c else "non_causal"): {

@@ -136,20 +136,20 @@ def workspace_views(ws, num_splits, B, H, Sq, d):
     return m, l, u
 
 
-def attn_block_m(d, dtype):
-    return int(_lib.load().attn_block_m(d, dtype))
+def attn_block_m(B, H, Sq, d, causal, dtype, num_splits=0):
+    return int(_lib.load().attn_block_m(B, H, Sq, d, int(causal), dtype, num_splits))
 
 
 def attn_block_n(d, dtype):
     return int(_lib.load().attn_block_n(d, dtype))
 
 
-def attn_num_workgroups(B, H, Sq, d, dtype, num_splits=1):
-    return int(_lib.load().attn_num_workgroups(B, H, Sq, d, dtype, num_splits))
+def attn_num_workgroups(B, H, Sq, d, causal, dtype, num_splits=0):
+    return int(_lib.load().attn_num_workgroups(B, H, Sq, d, int(causal), dtype, num_splits))
 
 
-def attn_kernel_name(d, dtype, splitkv=False):
-    return _lib.load().attn_kernel_name(d, dtype, int(bool(splitkv))).decode()
+def attn_kernel_name(B, H, Sq, d, causal, dtype, num_splits=0):
+    return _lib.load().attn_kernel_name(B, H, Sq, d, int(causal), dtype, num_splits).decode()
 
 
 def attn_status_string(status):

@@ -25,10 +25,10 @@ SIGNATURES = {
     "attn_fwd_splitkv": (_i, [_vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _i, _i, _f, _i, _i,
                               _f, _f, _f, _vp]),
     "attn_merge": (_i, [_vp, _sz, _i, _vp, _vp, _i, _i, _i, _i, _vp]),
-    "attn_block_m": (_i, [_i, _i]),
+    "attn_block_m": (_i, [_i, _i, _i, _i, _i, _i, _i]),
     "attn_block_n": (_i, [_i, _i]),
-    "attn_num_workgroups": (ctypes.c_int64, [_i, _i, _i, _i, _i, _i]),
-    "attn_kernel_name": (ctypes.c_char_p, [_i, _i, _i]),
+    "attn_num_workgroups": (ctypes.c_int64, [_i, _i, _i, _i, _i, _i, _i]),
+    "attn_kernel_name": (ctypes.c_char_p, [_i, _i, _i, _i, _i, _i, _i]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
     "attn_last_hip_error": (_i, []),
 }

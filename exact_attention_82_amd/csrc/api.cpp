@@ -1,8 +1,7 @@
 // C ABI of the attention library: argument checks, workspace layout and dispatch.
 //
 // Every check runs before anything is launched, so a refused call has no effect on the
-// outputs.  Nothing in this file touches the GPU; the launches live in
-// attn_kernels.hip.
+// outputs and makes no HIP call.  The launches live in attn_kernels.hip.
 #include <cmath>
 #include <cstdint>
 
@@ -31,7 +30,17 @@ attn_status check_shape(int B, int H, int Sq, int Sk, int d, int dtype) {
   const int64_t bh = int64_t(B) * H;
   if (bh * Sq * d >= kMaxIndex || bh * Sk * d >= kMaxIndex) return ATTN_ERR_SHAPE;
   if (bh * ceil_div(Sq, attn::kBlockM) >= (int64_t(1) << 31) / ATTN_MAX_SPLITS) return ATTN_ERR_SHAPE;
+  // One (batch, head) slice is addressed with 32-bit byte offsets, including the tile
+  // loads the key sweep issues past the end of the sequence (at most a few tiles).
+  const int64_t eb = dtype == ATTN_F32 ? 4 : dtype == ATTN_BF16 ? 2 : 1;
+  const int64_t longest = (Sq > Sk ? Sq : Sk) + attn::kMaxPrefetchKeys;
+  if (longest * d * eb >= (int64_t(1) << 31)) return ATTN_ERR_SHAPE;
   return ATTN_OK;
+}
+
+// Kernel plan of attn_fwd; only causal plans depend on the device (its CU count).
+attn::FwdPlan plan_for(int B, int H, int Sq, int d, int causal, int dtype) {
+  return attn::plan_fwd(B, H, Sq, d, causal, dtype, causal ? attn::device_cu_count() : 0);
 }
 
 attn_status launched(int hip_err) {
@@ -65,6 +74,8 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, float* o, floa
   a.num_splits = 1; a.chunk = Sk; a.split_mode = 0;
   a.scale_log2 = sl2;
   a.v_scale = 1.0f;
+  const attn::FwdPlan pl = plan_for(B, H, Sq, d, causal, dtype);
+  a.pair_order = pl.pair_order;
   return launched(attn::launch_fwd(a, stream));
 }
 
@@ -109,6 +120,7 @@ attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v,
   a.split_mode = 1;
   a.scale_log2 = sl2;
   a.v_scale = v_descale;
+  a.pair_order = 0;
   return launched(attn::launch_fwd(a, stream));
 }
 
@@ -134,9 +146,12 @@ attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o
   return launched(attn::launch_merge(a, stream));
 }
 
-int attn_block_m(int d, attn_dtype dtype) {
-  if (!supported_d(d) || !supported_dtype(dtype)) return 0;
-  return attn::kBlockM;
+int attn_block_m(int B, int H, int Sq, int d, int causal, attn_dtype dtype, int num_splits) {
+  if (B < 1 || H < 1 || Sq < 1 || !supported_d(d) || !supported_dtype(dtype)) return 0;
+  if (causal != 0 && causal != 1) return 0;
+  if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return 0;
+  if (num_splits >= 1) return attn::kBlockM;
+  return plan_for(B, H, Sq, d, causal, dtype).block_m;
 }
 
 int attn_block_n(int d, attn_dtype dtype) {
@@ -144,15 +159,17 @@ int attn_block_n(int d, attn_dtype dtype) {
   return attn::block_n(dtype, d);
 }
 
-int64_t attn_num_workgroups(int B, int H, int Sq, int d, attn_dtype dtype, int num_splits) {
-  if (B < 1 || H < 1 || Sq < 1 || !supported_d(d) || !supported_dtype(dtype)) return -1;
-  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return -1;
-  return int64_t(B) * H * ceil_div(Sq, attn::kBlockM) * num_splits;
+int64_t attn_num_workgroups(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
+                            int num_splits) {
+  const int bm = attn_block_m(B, H, Sq, d, causal, dtype, num_splits);
+  if (bm == 0) return -1;
+  return int64_t(B) * H * ceil_div(Sq, bm) * (num_splits >= 1 ? num_splits : 1);
 }
 
-const char* attn_kernel_name(int d, attn_dtype dtype, int splitkv) {
-  if (!supported_d(d) || !supported_dtype(dtype)) return "unsupported";
-  return attn::fwd_kernel_name(dtype, d, splitkv ? 1 : 0);
+const char* attn_kernel_name(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
+                             int num_splits) {
+  if (attn_block_m(B, H, Sq, d, causal, dtype, num_splits) == 0) return "unsupported";
+  return attn::fwd_kernel_name(dtype, d, num_splits >= 1 ? 1 : 0);
 }
 
 const char* attn_status_string(attn_status s) {

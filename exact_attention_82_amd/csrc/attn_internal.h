@@ -12,6 +12,7 @@ constexpr int kThreads = 256;     // 4 wavefronts of 64 lanes
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;  // query rows owned by one wavefront
 constexpr int kBlockM = 128;      // query rows per workgroup
+constexpr int kMaxPrefetchKeys = 512;  // keys past the end a sweep may request (ring depth)
 
 // Keys per tile of the key sweep, by element type and head dim.
 constexpr int block_n(int dtype, int d) {
@@ -35,7 +36,28 @@ struct FwdArgs {
   int split_mode; // 0: O and lse; 1: workspace states
   float scale_log2;  // scale * q_descale * k_descale * log2(e)
   float v_scale;     // v_descale
+  int pair_order;    // causal query-tile order: 0 longest first, 1 complementary pairs
 };
+
+// Launch plan of a forward call: query rows per workgroup and the causal tile order.
+struct FwdPlan {
+  int block_m;
+  int pair_order;
+};
+
+// Causal workgroups have key sweeps of very different lengths.  When the whole grid is
+// resident at once (at most `per_cu` workgroups per CU), workgroups i and i + grid/2
+// land on the same CU, so pairing query tile t with tile nqt-1-t gives every CU the
+// same work; otherwise the longest sweeps go first.
+inline FwdPlan plan_fwd(int B, int H, int Sq, int d, int causal, int dtype, int cus) {
+  FwdPlan pl{kBlockM, 0};
+  if (causal) {
+    const long long nwg = (long long)B * H * ((Sq + kBlockM - 1) / kBlockM);
+    const int per_cu = (d >= 256 || dtype == 0) ? 1 : 2;
+    pl.pair_order = (cus > 0 && nwg <= (long long)cus * per_cu) ? 1 : 0;
+  }
+  return pl;
+}
 
 struct MergeArgs {
   const float* ws_m;
@@ -66,6 +88,8 @@ inline WorkspaceLayout workspace_layout(int64_t rows, int d, int n) {
 // Launchers (attn_kernels.hip).  Return a hipError_t value as int.
 int launch_fwd(const FwdArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
+// Compute units of the current device (cached per device), or 0 if unknown.
+int device_cu_count();
 const char* fwd_kernel_name(int dtype, int d, int split_mode);
 
 }  // namespace attn

@@ -154,18 +154,18 @@ template <int DT, int D, int BN> struct DmaGeo {
   static constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
   static constexpr int TILE = BN * ROWB;               // bytes per tile (one stage)
   static constexpr int NI = TILE / 1024 / kWaves;      // 1 KiB loads per wavefront per tile
-  static constexpr int LDS_BYTES = 4 * TILE;           // 2 key stages + 2 value stages
-  static_assert(NI >= 1 && TILE % (1024 * kWaves) == 0, "tile must split into 1 KiB loads");
 };
 
 // Issue the loads of one tile (rows k0..k0+BN-1) straight into an LDS stage.
-template <int DT, int D, int BN, bool VALUE>
+template <int DT, int D, int BN, bool VALUE, int NW = kWaves>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint8_t* stage, int k0,
                                          int wave, int lane) {
   using G = DmaGeo<DT, D, BN>;
+  constexpr int NI = G::TILE / 1024 / NW;              // 1 KiB loads per wavefront
+  static_assert(NI >= 1 && G::TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads");
 #pragma unroll
-  for (int j = 0; j < G::NI; ++j) {
-    const int blk = wave * G::NI + j;                  // wave-uniform 1 KiB block
+  for (int j = 0; j < NI; ++j) {
+    const int blk = wave * NI + j;                     // wave-uniform 1 KiB block
     const int L = blk * 64 + lane;                     // chunk index inside the tile
     const int row = L / G::CPR, chp = L % G::CPR;
     const int ch = chp ^ (VALUE ? swz_v<DT, G::ROWB>(row) : swz_k<G::ROWB>(row));
@@ -261,6 +261,82 @@ __device__ __forceinline__ void pv_dma(f32x16_t (&oacc)[D / 32], const PTile<DT,
       }
     }
   }
+}
+
+
+// Operands of one tile read from LDS into registers ahead of their MFMAs, so that the
+// LDS latency is hidden behind other work and the MFMAs can issue back to back with
+// VALU work in between.
+template <int DT, int D, int BN> struct KOps {
+  typename Traits<DT>::Op a[D / 16][BN / 32];
+};
+template <int DT, int D, int BN> struct VOps {
+  typename Traits<DT>::Op a[BN / 32][2][D / 32];
+};
+
+template <int DT, int D, int BN>
+__device__ __forceinline__ void load_kops(KOps<DT, D, BN>& ko, const uint8_t* kt,
+                                          const DmaLane<DT, D, BN>& ln) {
+  using G = DmaGeo<DT, D, BN>;
+  using Op = typename Traits<DT>::Op;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int x = ln.kx ^ (DT == DT_BF16 ? (ks << 5) : (ks << 4));
+#pragma unroll
+    for (int b = 0; b < BN / 32; ++b) ko.a[ks][b] = *reinterpret_cast<const Op*>(kt + x + b * 32 * G::ROWB);
+  }
+}
+
+template <int DT, int D, int BN>
+__device__ __forceinline__ void load_vops(VOps<DT, D, BN>& vo, const uint8_t* vt,
+                                          const DmaLane<DT, D, BN>& ln) {
+  using G = DmaGeo<DT, D, BN>;
+  using Op = typename Traits<DT>::Op;
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int roff = (b * 32 + h * 16) * G::ROWB;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        if constexpr (DT == DT_BF16) {
+          const int dx = db << 6;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vt + roff + (ln.vx[0] ^ dx)));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vt + roff + (ln.vx[1] ^ dx)));
+          vo.a[b][h][db] = __builtin_bit_cast(Op, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2_t*)(vt + roff + (ln.vx[0] ^ (db << 5))));
+          vo.a[b][h][db] = __builtin_bit_cast(Op, v);
+        }
+      }
+    }
+}
+
+// S^T = K Q^T from key operands in registers.
+template <int DT, int D, int BN>
+__device__ __forceinline__ void qk_regs(f32x16_t (&s)[BN / 32], const KOps<DT, D, BN>& ko,
+                                        const typename Traits<DT>::Op (&qop)[D / 16]) {
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b) s[b] = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int b = 0; b < BN / 32; ++b) s[b] = Traits<DT>::mfma(ko.a[ks][b], qop[ks], s[b]);
+}
+
+// O^T += V^T P^T from value operands in registers.
+template <int DT, int D, int BN>
+__device__ __forceinline__ void pv_regs(f32x16_t (&oacc)[D / 32], const PTile<DT, BN>& pt,
+                                        const VOps<DT, D, BN>& vo) {
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = Traits<DT>::mfma(vo.a[b][h][db], pt.pk[b][h], oacc[db]);
 }
 
 // ================================================================== register-staged tiles (fp32)
@@ -367,17 +443,22 @@ template <int DT, int BN> struct PTile {
 };
 template <int BN> struct PTile<DT_F32, BN> {};
 
-// Online-softmax step for one tile: update the reference maximum (lazily), rescale the
-// accumulator when it moves, and produce the unnormalised probabilities
-// exp2(s * scale_log2 - m).  Two row sums are kept: l_run of the probabilities as
-// computed (it gives the log-sum-exp), and c_run of exactly the rounded values that
-// enter the value MFMA (it normalises O).  With c_run, numerator and denominator of O
-// agree, so a row dominated by one key returns that key's value up to accumulation
-// error instead of off by the rounding of its probability.
+// Online-softmax step for one tile, in three parts so that the key sweep can
+// interleave them with the MFMAs of neighbouring tiles:
+//
+//   softmax_rescale  row maximum; moves the reference maximum (lazily) and rescales
+//                    the accumulator and the running sums when it moves;
+//   softmax_exp      unnormalised probabilities exp2(s * scale_log2 - m), packed into
+//                    the operand form of the value MFMA;
+//   softmax_sums     two row sums: l_run of the probabilities as computed (it gives the
+//                    log-sum-exp), and c_run of exactly the rounded values that entered
+//                    the value MFMA (it normalises O).  With c_run, numerator and
+//                    denominator of O agree, so a row dominated by one key returns that
+//                    key's value up to accumulation error instead of off by the
+//                    rounding of its probability.
 template <int DT, int BN, int NDB>
-__device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], PTile<DT, BN>& pt,
-                                             f32x16_t (&oacc)[NDB], float& m_run, float& l_run,
-                                             float& c_run, float sl2) {
+__device__ __forceinline__ float softmax_rescale(const f32x16_t (&s)[BN / 32], f32x16_t (&oacc)[NDB],
+                                                 float& m_run, float& l_run, float& c_run, float sl2) {
   using TR = Traits<DT>;
   float mx = -__builtin_inff();
 #pragma unroll
@@ -395,38 +476,30 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], PTile<DT, B
     for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
     m_run = m_new;
   }
-  const float ms = (m_run == -__builtin_inff()) ? 0.0f : m_run;
-  float ls = 0.0f;
+  return (m_run == -__builtin_inff()) ? 0.0f : m_run;
+}
+
+template <int DT, int BN>
+__device__ __forceinline__ void softmax_exp(f32x16_t (&s)[BN / 32], PTile<DT, BN>& pt, float ms,
+                                            float sl2) {
+  using TR = Traits<DT>;
+  // FP8 probabilities come out scaled by kPScale = 2^8 (an exponent offset of 8).
+  const float mo = DT == DT_FP8 ? ms - 8.0f : ms;
 #pragma unroll
   for (int b = 0; b < BN / 32; ++b)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s[b][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][j], sl2, -ms));
-      ls += s[b][j];
-    }
-  l_run += ls;
+    for (int j = 0; j < 16; ++j) s[b][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][j], sl2, -mo));
   if constexpr (DT == DT_BF16) {
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float cs = 0.0f;
 #pragma unroll
     for (int b = 0; b < BN / 32; ++b)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         f32x8_t x = {s[b][8 * h + 0], s[b][8 * h + 1], s[b][8 * h + 2], s[b][8 * h + 3],
                      s[b][8 * h + 4], s[b][8 * h + 5], s[b][8 * h + 6], s[b][8 * h + 7]};
-        const bf16x8_t v = __builtin_convertvector(x, bf16x8_t);
-        pt.pk[b][h] = v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2_t two = {v[2 * e], v[2 * e + 1]};
-          cs = __builtin_amdgcn_fdot2_f32_bf16(two, ones, cs, false);
-        }
+        pt.pk[b][h] = __builtin_convertvector(x, bf16x8_t);
       }
-    c_run += cs;
   } else if constexpr (DT == DT_FP8) {
-    const float k = TR::kPScale;
-    float cs = 0.0f;
+    static_assert(TR::kPScale == 256.0f, "exponent offset above assumes 2^8");
 #pragma unroll
     for (int b = 0; b < BN / 32; ++b)
 #pragma unroll
@@ -435,19 +508,64 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], PTile<DT, B
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int e = 8 * h + 4 * q;
-          int v = __builtin_amdgcn_cvt_pk_fp8_f32(s[b][e + 0] * k, s[b][e + 1] * k, 0, false);
-          v = __builtin_amdgcn_cvt_pk_fp8_f32(s[b][e + 2] * k, s[b][e + 3] * k, v, true);
-          w[q] = v;
+          int v = __builtin_amdgcn_cvt_pk_fp8_f32(s[b][e + 0], s[b][e + 1], 0, false);
+          w[q] = __builtin_amdgcn_cvt_pk_fp8_f32(s[b][e + 2], s[b][e + 3], v, true);
+        }
+        pt.pk[b][h] = (long)(((unsigned long)(uint32_t)w[1] << 32) | (uint32_t)w[0]);
+      }
+  }
+}
+
+template <int DT, int BN>
+__device__ __forceinline__ void softmax_sums(const f32x16_t (&s)[BN / 32], const PTile<DT, BN>& pt,
+                                             float& l_run, float& c_run) {
+  using TR = Traits<DT>;
+  float ls = 0.0f;
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ls += s[b][j];
+  l_run += ls * (1.0f / TR::kPScale);
+  if constexpr (DT == DT_BF16) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float cs = 0.0f;
+#pragma unroll
+    for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2_t two = {pt.pk[b][h][2 * e], pt.pk[b][h][2 * e + 1]};
+          cs = __builtin_amdgcn_fdot2_f32_bf16(two, ones, cs, false);
+        }
+    c_run += cs;
+  } else if constexpr (DT == DT_FP8) {
+    float cs = 0.0f;
+#pragma unroll
+    for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int v = (int)(uint32_t)((unsigned long)pt.pk[b][h] >> (32 * q));
           const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
           const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
           cs += (lo[0] + lo[1]) + (hi[0] + hi[1]);
         }
-        pt.pk[b][h] = (long)(((unsigned long)(uint32_t)w[1] << 32) | (uint32_t)w[0]);
-      }
-    c_run += cs * (1.0f / k);
+    c_run += cs * (1.0f / TR::kPScale);
   } else {
     c_run += ls;
   }
+}
+
+template <int DT, int BN, int NDB>
+__device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], PTile<DT, BN>& pt,
+                                             f32x16_t (&oacc)[NDB], float& m_run, float& l_run,
+                                             float& c_run, float sl2) {
+  const float ms = softmax_rescale<DT, BN, NDB>(s, oacc, m_run, l_run, c_run, sl2);
+  softmax_exp<DT, BN>(s, pt, ms, sl2);
+  softmax_sums<DT, BN>(s, pt, l_run, c_run);
 }
 
 constexpr int waves_per_eu(int dt, int d) { return (d >= 256 || dt == DT_F32) ? 1 : 2; }
@@ -464,6 +582,8 @@ template <int DT, int D, int BN> struct Pipe<DT, D, BN, true> {
   static constexpr int STAGE_K = G::TILE, STAGE_V = G::TILE;
   static constexpr int NSTAGE = 4;
   static constexpr int KSTEPS = D / 16;
+  // Operands go LDS -> registers ahead of their MFMAs where the registers allow it.
+  static constexpr bool kRegOps = DT == DT_BF16 && D <= 128;
   // Wait until at most N iterations' worth of tile loads are still in flight.
   template <int N> __device__ __forceinline__ static void wait_loads() {
     constexpr int n = N * 2 * G::NI;  // key + value loads per thread per iteration
@@ -496,6 +616,7 @@ template <int DT, int D, int BN> struct Pipe<DT, D, BN, false> {
   static constexpr int STAGE_K = G::K_BYTES, STAGE_V = G::V_BYTES;
   static constexpr int NSTAGE = 2;
   static constexpr int KSTEPS = D / 2;
+  static constexpr bool kRegOps = false;
   template <int N> __device__ __forceinline__ static void wait_loads() { wait_vmem(); }
   StRegs<D, BN> rk, rv;
   int c, g;
@@ -516,6 +637,35 @@ template <int DT, int D, int BN> struct Pipe<DT, D, BN, false> {
     pv_st<D, BN>(oacc, s, vt, c, g);
   }
 };
+
+// ================================================================== instruction interleave
+// Within one wavefront an MFMA occupies the matrix pipe for 32 cycles (32x32x16) while
+// the wavefront keeps issuing independent VALU instructions, about four of them per
+// MFMA.  sched_pairs asks the scheduler for N repetitions of {C1 instructions of
+// class M1, C2 of class M2} (class masks of __builtin_amdgcn_sched_group_barrier:
+// 0x2 VALU, 0x8 MFMA), so the exponentials of one tile fill the shadow of the MFMAs of
+// its neighbours instead of running in a block of their own.
+template <int N, int M1, int C1, int M2, int C2>
+__device__ __forceinline__ void sched_pairs() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(M1, C1, 0);
+    __builtin_amdgcn_sched_group_barrier(M2, C2, 0);
+    sched_pairs<N - 1, M1, C1, M2, C2>();
+  }
+}
+
+// Interleave for one step of the key sweep: the S^T MFMAs of the next tile with the
+// exponentials and packing of this tile, then this tile's value MFMAs with its row sums.
+template <int DT, int D, int BN>
+__device__ __forceinline__ void interleave_step() {
+  constexpr int NKB = BN / 32;
+  constexpr int NQ = (D / 16) * NKB;          // S^T MFMAs
+  constexpr int NP = NKB * 2 * (D / 32);      // value MFMAs
+  constexpr int VE = NKB * (32 + 8);          // fma + exp per score, one convert per pair
+  constexpr int VS = NKB * (16 + 8);          // exact sum, consistent sum
+  sched_pairs<NQ, 0x8, 1, 0x2, (VE + NQ - 1) / NQ>();
+  sched_pairs<NP, 0x8, 1, 0x2, (VS + NP - 1) / NP>();
+}
 
 // ================================================================== forward kernel
 template <int DT, int D, int BN, bool SPLIT>
@@ -545,7 +695,17 @@ void attn_fwd_kernel(FwdArgs p) {
   x /= BH;
   int qt = x % nqt;
   const int split = x / nqt;
-  if (p.causal && !SPLIT) qt = nqt - 1 - qt;  // longest key sweeps first
+  if (p.causal && !SPLIT) {
+    if (p.pair_order) {
+      // The whole grid is resident at once (two workgroups per CU, dispatched in
+      // index order): workgroups i and i + grid/2 share a CU, so give them
+      // complementary query tiles (t and nqt-1-t) and every CU gets the same work.
+      const int half = (nqt + 1) / 2;
+      qt = qt < half ? nqt - 1 - qt : qt - half;
+    } else {
+      qt = nqt - 1 - qt;  // several rounds of workgroups: longest key sweeps first
+    }
+  }
   const int q0 = qt * kBlockM;
   const int r0 = q0 + wave * kRowsPerWave;    // first query row of this wavefront
   const int row = r0 + c;                     // query row of this lane
@@ -667,9 +827,25 @@ void attn_fwd_kernel(FwdArgs p) {
     pipe.issue_k(rk, k0 + NS * BN, kdst);
     pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
     PTile<DT, BN> pt;
-    pipe.qk(s_next, kb, qop);
-    softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
-    pipe.pv(oacc, s_cur, pt, vb);
+    if constexpr (P::kRegOps) {
+      // Both operand sets are read first (their LDS latency overlaps the row maximum),
+      // then the MFMAs of tile t+1 (S^T) and tile t (values) interleave with the
+      // exponentials and sums of tile t.
+      KOps<DT, D, BN> ko;
+      VOps<DT, D, BN> vo;
+      load_kops<DT, D, BN>(ko, kb, pipe.ln);
+      load_vops<DT, D, BN>(vo, vb, pipe.ln);
+      const float ms = softmax_rescale<DT, BN, NDB>(s_cur, oacc, m_run, l_run, c_run, sl2);
+      qk_regs<DT, D, BN>(s_next, ko, qop);
+      softmax_exp<DT, BN>(s_cur, pt, ms, sl2);
+      pv_regs<DT, D, BN>(oacc, pt, vo);
+      softmax_sums<DT, BN>(s_cur, pt, l_run, c_run);
+      interleave_step<DT, D, BN>();
+    } else {
+      pipe.qk(s_next, kb, qop);
+      softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
+      pipe.pv(oacc, s_cur, pt, vb);
+    }
     finish(kdst, vdst);
   };
   // Remaining tiles: the causal diagonal band, the sequence / chunk tail, the last tile.
@@ -763,6 +939,7 @@ void attn_fwd_kernel(FwdArgs p) {
     }
 }
 
+
 // ------------------------------------------------------------------ merge kernel
 // One group of D/4 lanes per row, each lane owning 4 consecutive columns.
 template <int D>
@@ -841,14 +1018,25 @@ int launch_merge(const MergeArgs& a, void* stream) {
   return int(hipGetLastError());
 }
 
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
 const char* fwd_kernel_name(int dtype, int d, int split_mode) {
   static const char* names[3][3][2] = {
       {{"attn_fwd_f32_d64_bm128_bn32", "attn_fwd_splitkv_f32_d64_bm128_bn32"},
        {"attn_fwd_f32_d128_bm128_bn32", "attn_fwd_splitkv_f32_d128_bm128_bn32"},
        {"attn_fwd_f32_d256_bm128_bn32", "attn_fwd_splitkv_f32_d256_bm128_bn32"}},
       {{"attn_fwd_bf16_d64_bm128_bn64", "attn_fwd_splitkv_bf16_d64_bm128_bn64"},
-       {"attn_fwd_bf16_d128_bm128_bn64", "attn_fwd_splitkv_bf16_d128_bm128_bn64"},
-       {"attn_fwd_bf16_d256_bm128_bn64", "attn_fwd_splitkv_bf16_d256_bm128_bn64"}},
+       {"attn_fwd_bf16_d128_bm128_bn32", "attn_fwd_splitkv_bf16_d128_bm128_bn32"},
+       {"attn_fwd_bf16_d256_bm128_bn32", "attn_fwd_splitkv_bf16_d256_bm128_bn32"}},
       {{"attn_fwd_fp8_d64_bm128_bn64", "attn_fwd_splitkv_fp8_d64_bm128_bn64"},
        {"attn_fwd_fp8_d128_bm128_bn64", "attn_fwd_splitkv_fp8_d128_bm128_bn64"},
        {"attn_fwd_fp8_d256_bm128_bn64", "attn_fwd_splitkv_fp8_d256_bm128_bn64"}}};

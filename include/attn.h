@@ -132,20 +132,26 @@ attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v,
 attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o, float* lse,
                        int B, int H, int Sq, int d, void* stream);
 
-/* Query rows per workgroup that attn_fwd / attn_fwd_splitkv use for (d, dtype), or 0. */
-int attn_block_m(int d, attn_dtype dtype);
+/*
+ * Launch plan queries.  num_splits = 0 describes attn_fwd; num_splits >= 1 describes
+ * attn_fwd_splitkv with that many chunks.  Every call launches one four-wavefront
+ * workgroup per 128 query rows (times num_splits); for causal attn_fwd calls the order
+ * of the query tiles over the grid depends on the current device's CU count (a HIP
+ * query), the grid size does not.
+ */
+/* Query rows per workgroup, or 0 if an argument is out of range. */
+int attn_block_m(int B, int H, int Sq, int d, int causal, attn_dtype dtype, int num_splits);
 
-/* Keys per tile of the key sweep for (d, dtype), or 0 if unsupported. */
+/* Keys per tile of the key sweep of the four-wavefront kernel for (d, dtype), or 0. */
 int attn_block_n(int d, attn_dtype dtype);
 
-/*
- * Number of workgroups one launch uses: B * H * ceil(Sq / block_m) * num_splits
- * (num_splits = 1 for attn_fwd), or -1 if an argument is out of range.
- */
-int64_t attn_num_workgroups(int B, int H, int Sq, int d, attn_dtype dtype, int num_splits);
+/* Workgroups of the launch: B * H * ceil(Sq / block_m) * max(1, num_splits), or -1. */
+int64_t attn_num_workgroups(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
+                            int num_splits);
 
-/* Name of the kernel instance a call with these arguments launches (static string). */
-const char* attn_kernel_name(int d, attn_dtype dtype, int splitkv);
+/* Name of the kernel instance the call launches (static string; "unsupported" if none). */
+const char* attn_kernel_name(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
+                             int num_splits);
 
 /* Human-readable text of a status code (static string). */
 const char* attn_status_string(attn_status s);

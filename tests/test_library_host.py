@@ -94,28 +94,40 @@ def test_workspace_layout(lib):
 
 
 def test_workgroup_count_follows_the_pages_query_tile_grid(lib):
-    """B * H * ceil(S / block_m): with block_m = 128 this is the 512 the page tabulates
-    for (1, 8, 8192); the (8, 32, 2048) shape gives 4096 (a line the page does not print)."""
+    """B * H * ceil(S / block_m), the query-tile grid the page tabulates.  Non-causal
+    plans need no device query, so this runs without a GPU: every dtype and head dim
+    uses 128 query rows per workgroup (the page's 512 workgroups for (1, 8, 8192)), and
+    so does the split-KV path, times the number of splits."""
     import json
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "cta_counts.json")))
     for dt in (0, 1, 2):
         for d in (64, 128, 256):
-            bm = lib.attn_block_m(d, dt)
+            bm = lib.attn_block_m(1, 8, 8192, d, 0, dt, 0)
             assert bm == 128
             for row in g["printed"]:
                 if row["tile_q"] == bm:
-                    got = lib.attn_num_workgroups(row["batch"], row["heads"], row["length"], d, dt, 1)
+                    got = lib.attn_num_workgroups(row["batch"], row["heads"], row["length"], d, 0, dt, 0)
                     assert got == row["ctas"]
-            assert lib.attn_num_workgroups(8, 32, 2048, d, dt, 1) == 4096
-            assert lib.attn_num_workgroups(1, 8, 128, d, dt, 16) == 8 * 16
-            assert lib.attn_num_workgroups(1, 16, 1000, d, dt, 1) == 16 * 8
-    assert lib.attn_num_workgroups(1, 8, 8192, 96, 1, 1) == -1
+            assert lib.attn_num_workgroups(8, 32, 2048, d, 0, dt, 0) == 8 * 32 * 2048 // bm
+            assert lib.attn_block_m(1, 8, 128, d, 0, dt, 16) == 128
+            assert lib.attn_num_workgroups(1, 8, 128, d, 0, dt, 16) == 8 * 16
+            assert lib.attn_num_workgroups(1, 8, 8192, d, 0, dt, 1) == 8 * 64
+            assert lib.attn_num_workgroups(1, 16, 1000, d, 0, dt, 0) == 16 * -(-1000 // bm)
+    assert lib.attn_num_workgroups(1, 8, 8192, 96, 0, 1, 0) == -1
+    assert lib.attn_block_m(1, 8, 8192, 128, 2, 1, 0) == 0
 
 
 def test_kernel_names_and_status_strings(lib):
-    assert lib.attn_kernel_name(128, 1, 0) == b"attn_fwd_bf16_d128_bm128_bn64"
-    assert lib.attn_kernel_name(128, 2, 1).startswith(b"attn_fwd_splitkv_fp8_d128")
-    assert lib.attn_kernel_name(100, 1, 0) == b"unsupported"
+    assert lib.attn_kernel_name(1, 8, 8192, 128, 0, 1, 0) == b"attn_fwd_bf16_d128_bm128_bn32"
+    assert lib.attn_kernel_name(1, 8, 8192, 256, 0, 1, 0) == b"attn_fwd_bf16_d256_bm128_bn32"
+    assert lib.attn_kernel_name(1, 8, 128, 128, 0, 2, 4).startswith(b"attn_fwd_splitkv_fp8_d128")
+    assert lib.attn_kernel_name(1, 8, 128, 100, 0, 1, 0) == b"unsupported"
     for s in range(8):
         assert lib.attn_status_string(s)
     assert lib.attn_last_hip_error() == 0
+
+
+def test_per_head_slices_must_fit_32bit_offsets(lib):
+    # 2^24 keys x 128 x bf16 = 4 GiB per head: refused before any launch
+    assert fwd(lib, Sq=8, Sk=1 << 24, d=128) == 2
+    assert fwd(lib, Sq=1 << 23, Sk=8, d=256, dtype=0) == 2
