@@ -66,6 +66,58 @@ def read_traffic():
         return None
 
 
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, f"*{suffix}"))):
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_stats(d: str) -> str:
+    """Markdown table of a `rocprofv3 --kernel-trace --stats` output directory."""
+    out = ["| kernel | calls | avg ns | min ns | max ns | % time |", "|---|---|---|---|---|---|"]
+    for r in _csv_rows(d, "_kernel_stats.csv"):
+        out.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                   f"{r['MaxNs']} | {r['Percentage']} |")
+    return "\n".join(out)
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, probe_mib: int, workload: str = "c3") -> str:
+    """HBM bytes per launch of the attention kernel from two `rocprofv3 --pmc` runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same counter
+    reads for the plain device copy of `probe_mib` MiB that `--copy-probe-mib` runs."""
+    B, H, S, d, _ = WORKLOADS[workload]
+    vals = {}
+    for name, dd in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _csv_rows(dd, "_counter_collection.csv") if r["Counter_Name"] == name]
+        kern = [float(r["Counter_Value"]) for r in rows if "attn_fwd_kernel" in r["Kernel_Name"]]
+        copies = sorted(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        probe = float(np.median(copies[-3:]))
+        vals[name] = (float(np.mean(kern)), len(kern), probe, probe_mib * 1024.0 / probe)
+        kname = next(r["Kernel_Name"] for r in rows if "attn_fwd_kernel" in r["Kernel_Name"])
+    rd = vals["FETCH_SIZE"][0] * vals["FETCH_SIZE"][3] * 1024
+    wr = vals["WRITE_SIZE"][0] * vals["WRITE_SIZE"][3] * 1024
+    alg = 3 * B * H * S * d * 2 + B * H * S * d * 4 + B * H * S * 4
+    return "\n".join([
+        f"kernel: {kname}",
+        f"kernel_source_sha256_16: {kernel_source_digest()}",
+        f"launches_measured: {vals['FETCH_SIZE'][1]}",
+        f"FETCH_SIZE_KiB_per_launch_raw: {vals['FETCH_SIZE'][0]:.1f}",
+        f"WRITE_SIZE_KiB_per_launch_raw: {vals['WRITE_SIZE'][0]:.1f}",
+        f"copy_probe_FETCH_SIZE_KiB_raw: {vals['FETCH_SIZE'][2]:.1f}",
+        f"copy_probe_WRITE_SIZE_KiB_raw: {vals['WRITE_SIZE'][2]:.1f}",
+        f"fetch_calibration_factor: {vals['FETCH_SIZE'][3]:.4f}",
+        f"write_calibration_factor: {vals['WRITE_SIZE'][3]:.4f}",
+        f"hbm_read_bytes_per_launch: {rd:.0f}",
+        f"hbm_write_bytes_per_launch: {wr:.0f}",
+        f"hbm_bytes_per_launch: {rd + wr:.0f}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic_over_algorithmic: {(rd + wr) / alg:.4f}",
+    ])
+
+
 def cpu_baseline(inp, scale, budget_s: float):
     """Time the fp64 oracle on whole heads of the same workload, both masks, head after
     head (cycling through the heads), until the time budget is used."""
@@ -107,7 +159,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--summarize-stats", metavar="DIR",
+                    help="print a table of a rocprofv3 --stats output directory and exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print HBM bytes per launch from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats))
+        return
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic, probe_mib=args.copy_probe_mib or 512,
+                                workload=args.workload))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

@@ -76,6 +76,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, float* o, floa
   a.v_scale = 1.0f;
   const attn::FwdPlan pl = plan_for(B, H, Sq, d, causal, dtype);
   a.pair_order = pl.pair_order;
+  a.head_group = pl.head_group;
   return launched(attn::launch_fwd(a, stream));
 }
 
@@ -121,6 +122,7 @@ attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v,
   a.scale_log2 = sl2;
   a.v_scale = v_descale;
   a.pair_order = 0;
+  a.head_group = attn::head_group(int64_t(B) * H, int((Sq + attn::kBlockM - 1) / attn::kBlockM));
   return launched(attn::launch_fwd(a, stream));
 }
 

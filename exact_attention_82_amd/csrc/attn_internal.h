@@ -37,20 +37,32 @@ struct FwdArgs {
   float scale_log2;  // scale * q_descale * k_descale * log2(e)
   float v_scale;     // v_descale
   int pair_order;    // causal query-tile order: 0 longest first, 1 complementary pairs
+  int head_group;    // heads whose query tiles are scheduled together (divides B*H)
 };
 
 // Launch plan of a forward call: query rows per workgroup and the causal tile order.
 struct FwdPlan {
   int block_m;
   int pair_order;
+  int head_group;
 };
 
 // Causal workgroups have key sweeps of very different lengths.  When the whole grid is
 // resident at once (at most `per_cu` workgroups per CU), workgroups i and i + grid/2
 // land on the same CU, so pairing query tile t with tile nqt-1-t gives every CU the
 // same work; otherwise the longest sweeps go first.
+//
+// head_group: the largest power of two dividing B*H whose query tiles (head_group *
+// ceil(Sq / 128) workgroups) fit in one XCD's resident set of 64 workgroups, so that
+// those workgroups share the heads' key/value tiles in the XCD's L2.
+inline int head_group(long long bh, int nqt) {
+  int g = 1;
+  while (bh % (2 * g) == 0 && (long long)(2 * g) * nqt <= 64) g *= 2;
+  return g;
+}
+
 inline FwdPlan plan_fwd(int B, int H, int Sq, int d, int causal, int dtype, int cus) {
-  FwdPlan pl{kBlockM, 0};
+  FwdPlan pl{kBlockM, 0, head_group((long long)B * H, (Sq + kBlockM - 1) / kBlockM)};
   if (causal) {
     const long long nwg = (long long)B * H * ((Sq + kBlockM - 1) / kBlockM);
     const int per_cu = (d >= 256 || dtype == 0) ? 1 : 2;

@@ -153,7 +153,6 @@ template <int DT, int D, int BN> struct DmaGeo {
   static constexpr int ROWB = D * EB;                  // bytes per row
   static constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
   static constexpr int TILE = BN * ROWB;               // bytes per tile (one stage)
-  static constexpr int NI = TILE / 1024 / kWaves;      // 1 KiB loads per wavefront per tile
 };
 
 // Issue the loads of one tile (rows k0..k0+BN-1) straight into an LDS stage.
@@ -568,15 +567,17 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], PTile<DT, B
   softmax_sums<DT, BN>(s, pt, l_run, c_run);
 }
 
+// Wavefronts per SIMD the register budget allows: two (256 registers each) unless a
+// wavefront holds a d = 256 accumulator or fp32 operands.
 constexpr int waves_per_eu(int dt, int d) { return (d >= 256 || dt == DT_F32) ? 1 : 2; }
 
 // ================================================================== tile pipeline
 // Uniform interface over the two ways tiles reach LDS.  issue_*: start the loads of a
 // tile (direct-to-LDS loads already target the stage); commit_*: registers -> LDS for
 // the staged variant, nothing for the direct one.
-template <int DT, int D, int BN, bool DMA = Traits<DT>::kDMA> struct Pipe;
+template <int DT, int D, int BN, int NW, bool DMA = Traits<DT>::kDMA> struct Pipe;
 
-template <int DT, int D, int BN> struct Pipe<DT, D, BN, true> {
+template <int DT, int D, int BN, int NW> struct Pipe<DT, D, BN, NW, true> {
   using G = DmaGeo<DT, D, BN>;
   using Op = typename Traits<DT>::Op;
   static constexpr int STAGE_K = G::TILE, STAGE_V = G::TILE;
@@ -585,8 +586,9 @@ template <int DT, int D, int BN> struct Pipe<DT, D, BN, true> {
   // Operands go LDS -> registers ahead of their MFMAs where the registers allow it.
   static constexpr bool kRegOps = DT == DT_BF16 && D <= 128;
   // Wait until at most N iterations' worth of tile loads are still in flight.
+  static constexpr int NI = G::TILE / 1024 / NW;  // 1 KiB loads per wavefront per tile
   template <int N> __device__ __forceinline__ static void wait_loads() {
-    constexpr int n = N * 2 * G::NI;  // key + value loads per thread per iteration
+    constexpr int n = N * 2 * NI;  // key + value loads per thread per iteration
     static_assert(n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
   }
@@ -594,10 +596,10 @@ template <int DT, int D, int BN> struct Pipe<DT, D, BN, true> {
   int wave, lane;
   __device__ __forceinline__ Pipe(int w, int l) : ln(l), wave(w), lane(l) {}
   __device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t rs, int k0, uint8_t* dst) {
-    dma_tile<DT, D, BN, false>(rs, dst, k0, wave, lane);
+    dma_tile<DT, D, BN, false, NW>(rs, dst, k0, wave, lane);
   }
   __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rs, int k0, uint8_t* dst) {
-    dma_tile<DT, D, BN, true>(rs, dst, k0, wave, lane);
+    dma_tile<DT, D, BN, true, NW>(rs, dst, k0, wave, lane);
   }
   __device__ __forceinline__ void commit_k(uint8_t*, int) {}
   __device__ __forceinline__ void commit_v(uint8_t*, int) {}
@@ -610,7 +612,8 @@ template <int DT, int D, int BN> struct Pipe<DT, D, BN, true> {
   }
 };
 
-template <int DT, int D, int BN> struct Pipe<DT, D, BN, false> {
+template <int DT, int D, int BN, int NW> struct Pipe<DT, D, BN, NW, false> {
+  static_assert(NW == kWaves, "the register-staged path runs four wavefronts");
   using G = StGeo<D, BN>;
   using Op = float;
   static constexpr int STAGE_K = G::K_BYTES, STAGE_V = G::V_BYTES;
@@ -673,7 +676,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(waves_per_eu(DT, D), waves_per_eu(DT, D))))
 void attn_fwd_kernel(FwdArgs p) {
   using TR = Traits<DT>;
-  using P = Pipe<DT, D, BN>;
+  using P = Pipe<DT, D, BN, kWaves>;
   using Op = typename TR::Op;
   constexpr int EB = TR::kBytes;
   constexpr int KSTEPS = D / TR::kKS;  // MFMAs over d per 32-key block of S^T
@@ -685,26 +688,39 @@ void attn_fwd_kernel(FwdArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, g = lane >> 5;
 
-  // ---- which (batch*head, query tile, split) this workgroup owns.  The linear index
-  // runs over batch*head fastest, so consecutive workgroups (which the dispatcher
-  // spreads over the XCDs round-robin) keep one head's key/value stream per XCD.
+  // ---- which (batch*head, query tile, split) this workgroup owns.
   const int BH = p.B * p.H;
   const int nqt = ceil_div_i(p.Sq, kBlockM);
-  int x = blockIdx.x;
-  const int bh = x % BH;
-  x /= BH;
-  int qt = x % nqt;
-  const int split = x / nqt;
-  if (p.causal && !SPLIT) {
-    if (p.pair_order) {
-      // The whole grid is resident at once (two workgroups per CU, dispatched in
-      // index order): workgroups i and i + grid/2 share a CU, so give them
-      // complementary query tiles (t and nqt-1-t) and every CU gets the same work.
-      const int half = (nqt + 1) / 2;
-      qt = qt < half ? nqt - 1 - qt : qt - half;
-    } else {
-      qt = nqt - 1 - qt;  // several rounds of workgroups: longest key sweeps first
-    }
+  int bh, qt, split;
+  if (!SPLIT && p.causal && p.pair_order) {
+    // The whole grid is resident at once (two workgroups per CU, dispatched in index
+    // order): workgroups i and i + grid/2 share a CU, so they get complementary query
+    // tiles (t and nqt-1-t) of the same head and every CU does the same work.  With
+    // batch*head fastest, all tiles of a head stay on one XCD (index mod 8).
+    int x = blockIdx.x;
+    bh = x % BH;
+    qt = x / BH;
+    split = 0;
+    const int half = (nqt + 1) / 2;
+    qt = qt < half ? nqt - 1 - qt : qt - half;
+  } else {
+    // The dispatcher hands workgroup i to XCD i mod 8.  Renumber so that each XCD
+    // works through a contiguous range of the logical order, and order that range as
+    // groups of head_group heads with all their query tiles, heads fastest: the
+    // workgroups resident on an XCD at one time then share a few heads' key/value
+    // streams in that XCD's L2.  Causal sweeps go longest first within each group.
+    int x = blockIdx.x;
+    const int nwg = gridDim.x;
+    if ((nwg & 7) == 0) x = (x & 7) * (nwg >> 3) + (x >> 3);
+    const int per_split = BH * nqt;
+    split = x / per_split;
+    x -= split * per_split;
+    const int G = p.head_group;
+    const int b = x % G;
+    x /= G;
+    const int r = x % nqt;
+    bh = (x / nqt) * G + b;
+    qt = (!SPLIT && p.causal) ? nqt - 1 - r : r;
   }
   const int q0 = qt * kBlockM;
   const int r0 = q0 + wave * kRowsPerWave;    // first query row of this wavefront
@@ -765,24 +781,31 @@ void attn_fwd_kernel(FwdArgs p) {
 
   P pipe(wave, lane);
   // NS-stage rings for key and value tiles.  Tile j lives in stage j % NS of each
-  // ring.  The sweep is unrolled by NS, so every LDS access names a compile-time
-  // stage and the direct-to-LDS loads still in flight provably do not alias the
-  // stages being read (no wait is needed before the operand reads).
+  // ring.  The sweep is unrolled, so every LDS access names a compile-time stage and
+  // the direct-to-LDS loads still in flight provably do not alias the stages being
+  // read (no wait is needed before the operand reads).
   constexpr int NS = P::NSTAGE;
-  static_assert(NS == 2 || NS == 4, "stage count");
+  static_assert(NS >= 2 && NS <= 5, "stage count");
   // one named array per stage: the wait insertion only tells distinct objects apart
   __shared__ __attribute__((aligned(1024))) uint8_t ks0[P::STAGE_K], ks1[P::STAGE_K];
   __shared__ __attribute__((aligned(1024))) uint8_t ks2[NS > 2 ? P::STAGE_K : 1];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks3[NS > 2 ? P::STAGE_K : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks3[NS > 3 ? P::STAGE_K : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks4[NS > 4 ? P::STAGE_K : 1];
   __shared__ __attribute__((aligned(1024))) uint8_t vs0[P::STAGE_V], vs1[P::STAGE_V];
   __shared__ __attribute__((aligned(1024))) uint8_t vs2[NS > 2 ? P::STAGE_V : 1];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs3[NS > 2 ? P::STAGE_V : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs3[NS > 3 ? P::STAGE_V : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs4[NS > 4 ? P::STAGE_V : 1];
   auto kst = [&](int j) __attribute__((always_inline)) -> uint8_t* {
-    return (j & 3) == 0 ? ks0 : (j & 3) == 1 ? ks1 : (j & 3) == 2 ? ks2 : ks3;
+    const int i = j % NS;
+    return i == 0 ? ks0 : i == 1 ? ks1 : i == 2 ? ks2 : i == 3 ? ks3 : ks4;
   };
   auto vst = [&](int j) __attribute__((always_inline)) -> uint8_t* {
-    return (j & 3) == 0 ? vs0 : (j & 3) == 1 ? vs1 : (j & 3) == 2 ? vs2 : vs3;
+    const int i = j % NS;
+    return i == 0 ? vs0 : i == 1 ? vs1 : i == 2 ? vs2 : i == 3 ? vs3 : vs4;
   };
+  // The sweep is unrolled by U tiles: a multiple of NS (constant stages) and of 2 (the
+  // two score buffers alternate).
+  constexpr int U = NS % 2 == 0 ? NS : 2 * NS;
 
   // ---- prologue: key tiles 0..NS-1 and value tiles 0..NS-2 in flight, then S^T of
   // tile 0 once key tile 0 has landed.  Loads are issued unconditionally (tiles past
@@ -802,8 +825,7 @@ void attn_fwd_kernel(FwdArgs p) {
   wait_vmem();
   block_sync();
   f32x16_t sa[NKB], sb[NKB];
-  bool act_cur = ntiles > 0 && active(kbeg);
-  if (act_cur) pipe.qk(sa, kst(0), qop);
+  if (ntiles > 0 && active(kbeg)) pipe.qk(sa, kst(0), qop);
   block_sync();
 
   // ---- key sweep.  Iteration t: S^T of tile t+1 is computed while tile t's softmax
@@ -866,8 +888,8 @@ void attn_fwd_kernel(FwdArgs p) {
     finish(kdst, vdst);
   };
   // Tiles [0, nfull) are full: start below every row's diagonal (causal) and end
-  // before kend; nfull is rounded down to a multiple of NS so that both loops start on
-  // stage 0 and the sweep stays unrolled by NS with constant stage indices.
+  // before kend; nfull is rounded down to a multiple of U so that both loops start on
+  // stage 0 with the first score buffer, unrolled with constant stage indices.
   int nfull = ntiles - 1;
   {
     const int lim_end = (kend - kbeg) / BN;  // tiles ending at or before kend
@@ -879,17 +901,17 @@ void attn_fwd_kernel(FwdArgs p) {
     }
     if (r0 >= p.Sq) nfull = 0;  // wavefronts with no row take the guarded path
     // Both loops pass one barrier per tile, so wavefronts may split at different tiles.
-    nfull = nfull < 0 ? 0 : (nfull / NS) * NS;
+    nfull = nfull < 0 ? 0 : (nfull / U) * U;
   }
   auto run = [&](auto full_c, int t0, int t1) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_c)::value;
-    for (int t = t0; t < t1; t += NS) {
+    for (int t = t0; t < t1; t += U) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
+      for (int j = 0; j < U; ++j) {
         if (t + j < t1) {
           uint8_t* kd = kst(j);
-          uint8_t* vd = vst((j + NS - 1) % NS);
-          const uint8_t* kb = kst((j + 1) % NS);
+          uint8_t* vd = vst(j + NS - 1);
+          const uint8_t* kb = kst(j + 1);
           const uint8_t* vb = vst(j);
           if (j % 2 == 0) {
             if constexpr (FULL) step_full(t + j, kd, vd, kb, vb, sa, sb);
