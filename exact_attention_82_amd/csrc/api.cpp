@@ -171,7 +171,8 @@ int64_t attn_num_workgroups(int B, int H, int Sq, int d, int causal, attn_dtype 
 const char* attn_kernel_name(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
                              int num_splits) {
   if (attn_block_m(B, H, Sq, d, causal, dtype, num_splits) == 0) return "unsupported";
-  return attn::fwd_kernel_name(dtype, d, num_splits >= 1 ? 1 : 0);
+  if (num_splits >= 1) return attn::fwd_kernel_name(dtype, d, 1, 0);
+  return attn::fwd_kernel_name(dtype, d, 0, plan_for(B, H, Sq, d, causal, dtype).pair_order == 2);
 }
 
 const char* attn_status_string(attn_status s) {

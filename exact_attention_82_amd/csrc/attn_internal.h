@@ -36,22 +36,22 @@ struct FwdArgs {
   int split_mode; // 0: O and lse; 1: workspace states
   float scale_log2;  // scale * q_descale * k_descale * log2(e)
   float v_scale;     // v_descale
-  int pair_order;    // causal query-tile order: 0 longest first, 1 complementary pairs
+  int pair_order;    // causal schedule: 0 longest first, 1 complementary tiles per CU,
+                     // 2 pairs of tiles shared by the two groups of one workgroup
   int head_group;    // heads whose query tiles are scheduled together (divides B*H)
 };
 
-// Launch plan of a forward call: query rows per workgroup and the causal tile order.
+// Launch plan of a forward call: query rows per workgroup and the causal schedule.
 struct FwdPlan {
   int block_m;
   int pair_order;
   int head_group;
 };
 
-// Causal workgroups have key sweeps of very different lengths.  When the whole grid is
-// resident at once (at most `per_cu` workgroups per CU), workgroups i and i + grid/2
-// land on the same CU, so pairing query tile t with tile nqt-1-t gives every CU the
-// same work; otherwise the longest sweeps go first.
-//
+// The causal pair kernel (two four-wavefront groups per workgroup sharing a pair of
+// query tiles) exists for bf16 with d <= 128: two rings of 64 KiB fit in the LDS.
+constexpr bool pairs_supported(int dtype, int d) { return dtype == 1 && d <= 128; }
+
 // head_group: the largest power of two dividing B*H whose query tiles (head_group *
 // ceil(Sq / 128) workgroups) fit in one XCD's resident set of 64 workgroups, so that
 // those workgroups share the heads' key/value tiles in the XCD's L2.
@@ -61,12 +61,24 @@ inline int head_group(long long bh, int nqt) {
   return g;
 }
 
+// Causal sweeps differ in length by up to nqt times.  In order of preference:
+//   2: one workgroup per pair of tiles (t, nqt-1-t) whose two groups split the pair's
+//      keys evenly, when one such workgroup per CU covers the grid;
+//   1: workgroups i and i + grid/2, which share a CU when the whole grid is resident
+//      (at most `per_cu` per CU), get complementary tiles t and nqt-1-t;
+//   0: longest sweeps first.
 inline FwdPlan plan_fwd(int B, int H, int Sq, int d, int causal, int dtype, int cus) {
-  FwdPlan pl{kBlockM, 0, head_group((long long)B * H, (Sq + kBlockM - 1) / kBlockM)};
-  if (causal) {
-    const long long nwg = (long long)B * H * ((Sq + kBlockM - 1) / kBlockM);
+  const long long bh = (long long)B * H;
+  const long long nqt = (Sq + kBlockM - 1) / kBlockM;
+  FwdPlan pl{kBlockM, 0, head_group(bh, (int)nqt)};
+  if (causal && cus > 0) {
     const int per_cu = (d >= 256 || dtype == 0) ? 1 : 2;
-    pl.pair_order = (cus > 0 && nwg <= (long long)cus * per_cu) ? 1 : 0;
+    if (pairs_supported(dtype, d) && bh * ((nqt + 1) / 2) <= cus) {
+      pl.pair_order = 2;
+      pl.block_m = 2 * kBlockM;
+    } else if (bh * nqt <= (long long)cus * per_cu) {
+      pl.pair_order = 1;
+    }
   }
   return pl;
 }
@@ -102,6 +114,6 @@ int launch_fwd(const FwdArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 // Compute units of the current device (cached per device), or 0 if unknown.
 int device_cu_count();
-const char* fwd_kernel_name(int dtype, int d, int split_mode);
+const char* fwd_kernel_name(int dtype, int d, int split_mode, int pairs);
 
 }  // namespace attn

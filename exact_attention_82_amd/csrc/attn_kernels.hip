@@ -671,13 +671,28 @@ __device__ __forceinline__ void interleave_step() {
 }
 
 // ================================================================== forward kernel
-template <int DT, int D, int BN, bool SPLIT>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+// MODE kPlain: O and lse of one 128-row query tile per workgroup (four wavefronts).
+// MODE kSplit: the unnormalised state of one key chunk of one query tile.
+// MODE kPairs (causal): one workgroup of two four-wavefront groups per pair of query
+//   tiles t < T = nqt-1-t of one head, which together need (t+1) + (T+1) key-tile
+//   units.  Group A sweeps tile t, then the first X key tiles of tile T; group B
+//   sweeps the rest of tile T; X is chosen so that both groups sweep the same number
+//   of key tiles.  At the end A hands its partial state of tile T to B through LDS and
+//   B merges the two (the split-K merge of the pages, inside one workgroup).  Every CU
+//   then does the same work with both groups busy to the end, where separate
+//   workgroups of very different lengths would leave one alone on its CU.
+enum : int { kPlain = 0, kSplit = 1, kPairs = 2 };
+
+template <int DT, int D, int BN, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads * (MODE == kPairs ? 2 : 1),
+                                                      kThreads * (MODE == kPairs ? 2 : 1)),
                           amdgpu_waves_per_eu(waves_per_eu(DT, D), waves_per_eu(DT, D))))
 void attn_fwd_kernel(FwdArgs p) {
   using TR = Traits<DT>;
   using P = Pipe<DT, D, BN, kWaves>;
   using Op = typename TR::Op;
+  constexpr bool SPLIT = MODE == kSplit;
+  constexpr int NG = MODE == kPairs ? 2 : 1;  // four-wavefront groups per workgroup
   constexpr int EB = TR::kBytes;
   constexpr int KSTEPS = D / TR::kKS;  // MFMAs over d per 32-key block of S^T
   constexpr int NKB = BN / 32;         // 32-key blocks per tile
@@ -685,22 +700,26 @@ void attn_fwd_kernel(FwdArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gwave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = NG > 1 ? gwave / kWaves : 0;      // group of this wavefront
+  const int wave = NG > 1 ? gwave % kWaves : gwave;  // wavefront within its group
+  const int gtid = NG > 1 ? tid % kThreads : tid;    // thread within its group
   const int c = lane & 31, g = lane >> 5;
 
-  // ---- which (batch*head, query tile, split) this workgroup owns.
+  // ---- which (batch*head, query tile(s), split) this workgroup owns.
   const int BH = p.B * p.H;
   const int nqt = ceil_div_i(p.Sq, kBlockM);
-  int bh, qt, split;
-  if (!SPLIT && p.causal && p.pair_order) {
+  int bh, qt, split = 0;
+  if (MODE == kPairs) {
+    // batch*head fastest: all pairs of a head land on one XCD (index mod 8).
+    bh = blockIdx.x % BH;
+    qt = blockIdx.x / BH;              // the lighter tile t of the pair
+  } else if (!SPLIT && p.causal && p.pair_order) {
     // The whole grid is resident at once (two workgroups per CU, dispatched in index
     // order): workgroups i and i + grid/2 share a CU, so they get complementary query
-    // tiles (t and nqt-1-t) of the same head and every CU does the same work.  With
-    // batch*head fastest, all tiles of a head stay on one XCD (index mod 8).
-    int x = blockIdx.x;
-    bh = x % BH;
-    qt = x / BH;
-    split = 0;
+    // tiles (t and nqt-1-t) of the same head and every CU gets the same work.
+    bh = blockIdx.x % BH;
+    qt = blockIdx.x / BH;
     const int half = (nqt + 1) / 2;
     qt = qt < half ? nqt - 1 - qt : qt - half;
   } else {
@@ -722,25 +741,14 @@ void attn_fwd_kernel(FwdArgs p) {
     bh = (x / nqt) * G + b;
     qt = (!SPLIT && p.causal) ? nqt - 1 - r : r;
   }
-  const int q0 = qt * kBlockM;
-  const int r0 = q0 + wave * kRowsPerWave;    // first query row of this wavefront
-  const int row = r0 + c;                     // query row of this lane
   const int off = p.Sk - p.Sq;                // causal: key j visible to row i iff j <= i + off
-  const int wave_last = min(r0 + kRowsPerWave - 1, p.Sq - 1);
 
-  int kbeg = 0, kend = p.Sk;
-  if (SPLIT) {
-    const long long b = (long long)split * p.chunk;
-    kbeg = (int)(b < p.Sk ? b : p.Sk);
-    const long long e = b + p.chunk;
-    kend = (int)(e < p.Sk ? e : p.Sk);
-  }
-  int kend_wg = kend;
-  if (p.causal) {
-    const int last_row = min(q0 + kBlockM, p.Sq) - 1;
-    kend_wg = min(kend, last_row + off + 1);
-  }
-  const int ntiles = kend_wg > kbeg ? ceil_div_i(kend_wg - kbeg, BN) : 0;
+  // Keys a query tile sees: [0, kend_of(tile)) (causal: up to its last row's diagonal).
+  auto kend_of = [&](int tile) __attribute__((always_inline)) {
+    if (!p.causal) return p.Sk;
+    const int last_row = min((tile + 1) * kBlockM, p.Sq) - 1;
+    return max(0, min(p.Sk, last_row + off + 1));
+  };
 
   const size_t q_base = size_t(bh) * p.Sq * D;
   const size_t kv_base = size_t(bh) * p.Sk * D;
@@ -751,214 +759,325 @@ void attn_fwd_kernel(FwdArgs p) {
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + kv_base * EB,
                                               uint32_t(p.Sk) * D * EB);
 
-  // ---- Q operands for the whole sweep, in registers (B operand of S^T = K Q^T);
-  // rows past Sq read as zeros.
+  // ---- per-wavefront state of the query tile being swept
+  int q0 = 0, r0 = 0, row = 0, wave_last = 0;
   Op qop[KSTEPS];
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    const int boff = (row * D + ks * TR::kKS + g * TR::kKPL) * EB;
-    if constexpr (DT == DT_BF16) {
-      qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b128(rq, boff, 0, 0));
-    } else if constexpr (DT == DT_FP8) {
-      qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b64(rq, boff, 0, 0));
-    } else {
-      qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b32(rq, boff, 0, 0));
-    }
-  }
-
   f32x16_t oacc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16_t{};
-  float m_run = -__builtin_inff();  // reference maximum, log2 units (same in lanes c, c+32)
-  float l_run = 0.0f;               // this lane's share of the row sum
-  float c_run = 0.0f;               // same, of the probabilities as rounded for the MFMA
+  float m_run, l_run, c_run;  // reference maximum (log2 units), row sum, consistent row sum
   const float sl2 = p.scale_log2;
 
-  // A tile starting at key k0 has work for this wavefront unless every row of the
-  // wavefront is past Sq or (causal) every key of the tile is above its diagonal.
-  auto active = [&](int k0) __attribute__((always_inline)) { return r0 < p.Sq && (!p.causal || k0 <= wave_last + off); };
-  auto needs_mask = [&](int k0) __attribute__((always_inline)) { return (k0 + BN > kend) || (p.causal && (k0 + BN - 1 > r0 + off)); };
+  // Start query tile `tile`: its rows, its Q operands (B operand of S^T = K Q^T, in
+  // registers for the whole sweep; rows past Sq read as zeros) and an empty state.
+  auto begin_tile = [&](int tile) __attribute__((always_inline)) {
+    q0 = tile * kBlockM;
+    r0 = q0 + wave * kRowsPerWave;            // first query row of this wavefront
+    row = r0 + c;                             // query row of this lane
+    wave_last = min(r0 + kRowsPerWave - 1, p.Sq - 1);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int boff = (row * D + ks * TR::kKS + g * TR::kKPL) * EB;
+      if constexpr (DT == DT_BF16) {
+        qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b128(rq, boff, 0, 0));
+      } else if constexpr (DT == DT_FP8) {
+        qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b64(rq, boff, 0, 0));
+      } else {
+        qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b32(rq, boff, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[i] = f32x16_t{};
+    m_run = -__builtin_inff();  // same in lanes c and c+32
+    l_run = 0.0f;               // this lane's share of the row sum
+    c_run = 0.0f;               // same, of the probabilities as rounded for the MFMA
+  };
 
   P pipe(wave, lane);
-  // NS-stage rings for key and value tiles.  Tile j lives in stage j % NS of each
-  // ring.  The sweep is unrolled, so every LDS access names a compile-time stage and
-  // the direct-to-LDS loads still in flight provably do not alias the stages being
-  // read (no wait is needed before the operand reads).
+  // NS-stage rings for key and value tiles, one pair of rings per group.  Tile j lives
+  // in stage j % NS.  The sweep is unrolled, so every LDS access names a compile-time
+  // stage and the direct-to-LDS loads still in flight provably do not alias the
+  // stages being read (no wait is needed before the operand reads).
   constexpr int NS = P::NSTAGE;
   static_assert(NS >= 2 && NS <= 5, "stage count");
+  constexpr int SK = P::STAGE_K * NG, SV = P::STAGE_V * NG;
   // one named array per stage: the wait insertion only tells distinct objects apart
-  __shared__ __attribute__((aligned(1024))) uint8_t ks0[P::STAGE_K], ks1[P::STAGE_K];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks2[NS > 2 ? P::STAGE_K : 1];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks3[NS > 3 ? P::STAGE_K : 1];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks4[NS > 4 ? P::STAGE_K : 1];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs0[P::STAGE_V], vs1[P::STAGE_V];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs2[NS > 2 ? P::STAGE_V : 1];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs3[NS > 3 ? P::STAGE_V : 1];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs4[NS > 4 ? P::STAGE_V : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[SK], ks1[SK];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks2[NS > 2 ? SK : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks3[NS > 3 ? SK : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks4[NS > 4 ? SK : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[SV], vs1[SV];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs2[NS > 2 ? SV : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs3[NS > 3 ? SV : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs4[NS > 4 ? SV : 1];
+  const int kgo = grp * P::STAGE_K, vgo = grp * P::STAGE_V;  // this group's half
   auto kst = [&](int j) __attribute__((always_inline)) -> uint8_t* {
     const int i = j % NS;
-    return i == 0 ? ks0 : i == 1 ? ks1 : i == 2 ? ks2 : i == 3 ? ks3 : ks4;
+    return (i == 0 ? ks0 : i == 1 ? ks1 : i == 2 ? ks2 : i == 3 ? ks3 : ks4) + kgo;
   };
   auto vst = [&](int j) __attribute__((always_inline)) -> uint8_t* {
     const int i = j % NS;
-    return i == 0 ? vs0 : i == 1 ? vs1 : i == 2 ? vs2 : i == 3 ? vs3 : vs4;
+    return (i == 0 ? vs0 : i == 1 ? vs1 : i == 2 ? vs2 : i == 3 ? vs3 : vs4) + vgo;
   };
   // The sweep is unrolled by U tiles: a multiple of NS (constant stages) and of 2 (the
   // two score buffers alternate).
   constexpr int U = NS % 2 == 0 ? NS : 2 * NS;
 
-  // ---- prologue: key tiles 0..NS-1 and value tiles 0..NS-2 in flight, then S^T of
-  // tile 0 once key tile 0 has landed.  Loads are issued unconditionally (tiles past
-  // the end read as zeros and are never used) so that every iteration has the same
-  // number of loads in flight and the partial waits below stay exact.
-  if (ntiles > 0) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      pipe.issue_k(rk, kbeg + j * BN, kst(j));
-      pipe.commit_k(kst(j), tid);
-      if (j < NS - 1) {
-        pipe.issue_v(rv, kbeg + j * BN, vst(j));
-        pipe.commit_v(vst(j), tid);
-      }
-    }
-  }
-  wait_vmem();
-  block_sync();
-  f32x16_t sa[NKB], sb[NKB];
-  if (ntiles > 0 && active(kbeg)) pipe.qk(sa, kst(0), qop);
-  block_sync();
+  // ---- key sweep over keys [kbeg, kend) of the current query tile, in `ntiles`
+  // iterations.  Every group of the workgroup passes the same number of barriers
+  // (2 + ntiles): iterations past this group's own keys only keep the barrier cadence.
+  auto sweep = [&](int kbeg, int kend, int ntiles) __attribute__((always_inline)) {
+    // A tile starting at key k0 has work for this wavefront unless it starts past the
+    // range, every row of the wavefront is past Sq, or (causal) every key of the tile
+    // is above the wavefront's diagonal.
+    auto active = [&](int k0) __attribute__((always_inline)) {
+      return k0 < kend && r0 < p.Sq && (!p.causal || k0 <= wave_last + off);
+    };
+    auto needs_mask = [&](int k0) __attribute__((always_inline)) {
+      return (k0 + BN > kend) || (p.causal && (k0 + BN - 1 > r0 + off));
+    };
 
-  // ---- key sweep.  Iteration t: S^T of tile t+1 is computed while tile t's softmax
-  // runs; then O^T += V^T P^T with tile t's values.  Key tile t+NS and value tile
-  // t+NS-1 are requested into the stages that iteration t-1 finished reading; at the
-  // end of the iteration only the loads that iteration t+1 needs are waited for.
-  auto finish = [&](uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
-    pipe.commit_k(kdst, tid);
-    pipe.commit_v(vdst, tid);
-    // Loads complete in order and every iteration issues the same number, so leaving
-    // the newest (NS-2) iterations' loads in flight guarantees that key tile t+2 and
-    // value tile t+1 have landed.
-    P::template wait_loads<NS - 2>();
-    block_sync();
-  };
-  // Main part: tiles with a successor that are visible to every row of the workgroup
-  // (no mask, every wavefront active).  One straight-line block per tile.
-  auto step_full = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
-                       f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB]) __attribute__((always_inline)) {
-    const int k0 = kbeg + t * BN;
-    pipe.issue_k(rk, k0 + NS * BN, kdst);
-    pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
-    PTile<DT, BN> pt;
-    if constexpr (P::kRegOps) {
-      // Both operand sets are read first (their LDS latency overlaps the row maximum),
-      // then the MFMAs of tile t+1 (S^T) and tile t (values) interleave with the
-      // exponentials and sums of tile t.
-      KOps<DT, D, BN> ko;
-      VOps<DT, D, BN> vo;
-      load_kops<DT, D, BN>(ko, kb, pipe.ln);
-      load_vops<DT, D, BN>(vo, vb, pipe.ln);
-      const float ms = softmax_rescale<DT, BN, NDB>(s_cur, oacc, m_run, l_run, c_run, sl2);
-      qk_regs<DT, D, BN>(s_next, ko, qop);
-      softmax_exp<DT, BN>(s_cur, pt, ms, sl2);
-      pv_regs<DT, D, BN>(oacc, pt, vo);
-      softmax_sums<DT, BN>(s_cur, pt, l_run, c_run);
-      interleave_step<DT, D, BN>();
-    } else {
-      pipe.qk(s_next, kb, qop);
-      softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
-      pipe.pv(oacc, s_cur, pt, vb);
-    }
-    finish(kdst, vdst);
-  };
-  // Remaining tiles: the causal diagonal band, the sequence / chunk tail, the last tile.
-  auto step_edge = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
-                       f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB]) __attribute__((always_inline)) {
-    const int k0 = kbeg + t * BN;
-    const bool act_cur = active(k0);
-    const bool act_next = t + 1 < ntiles && active(k0 + BN);
-    pipe.issue_k(rk, k0 + NS * BN, kdst);
-    pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
-    if (act_next) pipe.qk(s_next, kb, qop);
-    if (act_cur) {
-      if (needs_mask(k0)) mask_tile<BN>(s_cur, k0, kend, row, off, p.causal, g);
-      PTile<DT, BN> pt;
-      softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
-      pipe.pv(oacc, s_cur, pt, vb);
-    }
-    finish(kdst, vdst);
-  };
-  // Tiles [0, nfull) are full: start below every row's diagonal (causal) and end
-  // before kend; nfull is rounded down to a multiple of U so that both loops start on
-  // stage 0 with the first score buffer, unrolled with constant stage indices.
-  int nfull = ntiles - 1;
-  {
-    const int lim_end = (kend - kbeg) / BN;  // tiles ending at or before kend
-    nfull = min(nfull, lim_end);
-    if (p.causal) {
-      // tile t is fully visible to the workgroup's first row iff k0 + BN - 1 <= q0 + off
-      const int d = q0 + off - kbeg - (BN - 1);
-      nfull = min(nfull, d < 0 ? 0 : d / BN + 1);
-    }
-    if (r0 >= p.Sq) nfull = 0;  // wavefronts with no row take the guarded path
-    // Both loops pass one barrier per tile, so wavefronts may split at different tiles.
-    nfull = nfull < 0 ? 0 : (nfull / U) * U;
-  }
-  auto run = [&](auto full_c, int t0, int t1) __attribute__((always_inline)) {
-    constexpr bool FULL = decltype(full_c)::value;
-    for (int t = t0; t < t1; t += U) {
+    // prologue: key tiles 0..NS-1 and value tiles 0..NS-2 in flight, then S^T of tile
+    // 0 once key tile 0 has landed.  Loads are issued unconditionally (tiles past the
+    // end are never used; past the sequence they read as zeros) so that every
+    // iteration has the same number of loads in flight and the partial waits stay
+    // exact.
+    if (ntiles > 0) {
 #pragma unroll
-      for (int j = 0; j < U; ++j) {
-        if (t + j < t1) {
-          uint8_t* kd = kst(j);
-          uint8_t* vd = vst(j + NS - 1);
-          const uint8_t* kb = kst(j + 1);
-          const uint8_t* vb = vst(j);
-          if (j % 2 == 0) {
-            if constexpr (FULL) step_full(t + j, kd, vd, kb, vb, sa, sb);
-            else step_edge(t + j, kd, vd, kb, vb, sa, sb);
-          } else {
-            if constexpr (FULL) step_full(t + j, kd, vd, kb, vb, sb, sa);
-            else step_edge(t + j, kd, vd, kb, vb, sb, sa);
-          }
+      for (int j = 0; j < NS; ++j) {
+        pipe.issue_k(rk, kbeg + j * BN, kst(j));
+        pipe.commit_k(kst(j), gtid);
+        if (j < NS - 1) {
+          pipe.issue_v(rv, kbeg + j * BN, vst(j));
+          pipe.commit_v(vst(j), gtid);
         }
       }
     }
+    wait_vmem();
+    block_sync();
+    f32x16_t sa[NKB], sb[NKB];
+    if (ntiles > 0 && active(kbeg)) pipe.qk(sa, kst(0), qop);
+    block_sync();
+
+    // Iteration t: S^T of tile t+1 is computed while tile t's softmax runs; then
+    // O^T += V^T P^T with tile t's values.  Key tile t+NS and value tile t+NS-1 are
+    // requested into the stages that iteration t-1 finished reading; at the end of
+    // the iteration only the loads that iteration t+1 needs are waited for.
+    auto finish = [&](uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
+      pipe.commit_k(kdst, gtid);
+      pipe.commit_v(vdst, gtid);
+      // Loads complete in order and every iteration issues the same number, so
+      // leaving the newest (NS-2) iterations' loads in flight guarantees that key
+      // tile t+2 and value tile t+1 have landed.
+      P::template wait_loads<NS - 2>();
+      block_sync();
+    };
+    // Main part: tiles with a successor that are visible to every row of the group
+    // (no mask, every wavefront active).  One straight-line block per tile.
+    auto step_full = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
+                         f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB]) __attribute__((always_inline)) {
+      const int k0 = kbeg + t * BN;
+      pipe.issue_k(rk, k0 + NS * BN, kdst);
+      pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
+      PTile<DT, BN> pt;
+      if constexpr (P::kRegOps) {
+        // Both operand sets are read first (their LDS latency overlaps the row
+        // maximum), then the MFMAs of tile t+1 (S^T) and tile t (values) interleave
+        // with the exponentials and sums of tile t.
+        KOps<DT, D, BN> ko;
+        VOps<DT, D, BN> vo;
+        load_kops<DT, D, BN>(ko, kb, pipe.ln);
+        load_vops<DT, D, BN>(vo, vb, pipe.ln);
+        const float ms = softmax_rescale<DT, BN, NDB>(s_cur, oacc, m_run, l_run, c_run, sl2);
+        qk_regs<DT, D, BN>(s_next, ko, qop);
+        softmax_exp<DT, BN>(s_cur, pt, ms, sl2);
+        pv_regs<DT, D, BN>(oacc, pt, vo);
+        softmax_sums<DT, BN>(s_cur, pt, l_run, c_run);
+        interleave_step<DT, D, BN>();
+      } else {
+        pipe.qk(s_next, kb, qop);
+        softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
+        pipe.pv(oacc, s_cur, pt, vb);
+      }
+      finish(kdst, vdst);
+    };
+    // Remaining tiles: the causal diagonal band, the sequence / chunk tail, the last
+    // tile, and the cadence-keeping iterations past the range.
+    auto step_edge = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
+                         f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB]) __attribute__((always_inline)) {
+      const int k0 = kbeg + t * BN;
+      const bool act_cur = active(k0);
+      const bool act_next = t + 1 < ntiles && active(k0 + BN);
+      pipe.issue_k(rk, k0 + NS * BN, kdst);
+      pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
+      if (act_next) pipe.qk(s_next, kb, qop);
+      if (act_cur) {
+        if (needs_mask(k0)) mask_tile<BN>(s_cur, k0, kend, row, off, p.causal, g);
+        PTile<DT, BN> pt;
+        softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
+        pipe.pv(oacc, s_cur, pt, vb);
+      }
+      finish(kdst, vdst);
+    };
+    // Tiles [0, nfull) are full: below every row's diagonal (causal) and before kend;
+    // nfull is rounded down to a multiple of U so that both loops start on stage 0
+    // with the first score buffer, unrolled with constant stage indices.
+    int nfull = ntiles - 1;
+    {
+      const int lim_end = (kend - kbeg) / BN;  // tiles ending at or before kend
+      nfull = min(nfull, lim_end);
+      if (p.causal) {
+        // tile t is fully visible to the tile's first row iff k0 + BN - 1 <= q0 + off
+        const int d = q0 + off - kbeg - (BN - 1);
+        nfull = min(nfull, d < 0 ? 0 : d / BN + 1);
+      }
+      if (r0 >= p.Sq) nfull = 0;  // wavefronts with no row take the guarded path
+      // Both loops pass one barrier per tile, so wavefronts may split at different tiles.
+      nfull = nfull < 0 ? 0 : (nfull / U) * U;
+    }
+    auto run = [&](auto full_c, int t0, int t1) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full_c)::value;
+      for (int t = t0; t < t1; t += U) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          if (t + j < t1) {
+            uint8_t* kd = kst(j);
+            uint8_t* vd = vst(j + NS - 1);
+            const uint8_t* kb = kst(j + 1);
+            const uint8_t* vb = vst(j);
+            if (j % 2 == 0) {
+              if constexpr (FULL) step_full(t + j, kd, vd, kb, vb, sa, sb);
+              else step_edge(t + j, kd, vd, kb, vb, sa, sb);
+            } else {
+              if constexpr (FULL) step_full(t + j, kd, vd, kb, vb, sb, sa);
+              else step_edge(t + j, kd, vd, kb, vb, sb, sa);
+            }
+          }
+        }
+      }
+    };
+    run(std::true_type{}, 0, nfull);
+    run(std::false_type{}, nfull, ntiles);
+    // Drain every load before the rings are reused, by this group or the next sweep.
+    wait_vmem();
+    block_sync();
   };
-  run(std::true_type{}, 0, nfull);
-  run(std::false_type{}, nfull, ntiles);
-  wait_vmem();
 
   // ---- write-back: deferred normalisation
-  const float l_tot = pair_sum(l_run);
-  const float c_tot = pair_sum(c_run);
-  if (row >= p.Sq) return;
-  const size_t ridx = size_t(bh) * p.Sq + row;
-  float* out;
-  float sc;
-  if constexpr (!SPLIT) {
-    out = p.o + ridx * D;
-    sc = c_tot > 0.0f ? p.v_scale / (TR::kPScale * c_tot) : 0.0f;
-    if (g == 0)
-      p.lse[ridx] = l_tot > 0.0f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
+  auto write_out = [&]() __attribute__((always_inline)) {
+    const float l_tot = pair_sum(l_run);
+    const float c_tot = pair_sum(c_run);
+    if (row >= p.Sq) return;
+    const size_t ridx = size_t(bh) * p.Sq + row;
+    float* out;
+    float sc;
+    if constexpr (!SPLIT) {
+      out = p.o + ridx * D;
+      sc = c_tot > 0.0f ? p.v_scale / (TR::kPScale * c_tot) : 0.0f;
+      if (g == 0)
+        p.lse[ridx] = l_tot > 0.0f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
+    } else {
+      // u is stored as (l / c) * sum(rounded p * v): u / l is then the chunk's
+      // consistent weighted average, while u still equals sum(exp(s - m) v) up to
+      // rounding.
+      const size_t sidx = size_t(split) * size_t(BH) * p.Sq + ridx;
+      out = p.ws_u + sidx * D;
+      sc = c_tot > 0.0f ? p.v_scale * l_tot / (TR::kPScale * c_tot) : 0.0f;
+      if (g == 0) {
+        p.ws_m[sidx] = l_tot > 0.0f ? m_run * kLn2 : -__builtin_inff();
+        p.ws_l[sidx] = l_tot;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x4_t v4 = {oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2],
+                      oacc[db][4 * jj + 3]};
+        *reinterpret_cast<f32x4_t*>(out + db * 32 + jj * 8 + g * 4) = v4 * sc;
+      }
+  };
+
+  if constexpr (MODE != kPairs) {
+    int kbeg = 0, kend = p.Sk;
+    if (SPLIT) {
+      const long long b = (long long)split * p.chunk;
+      kbeg = (int)(b < p.Sk ? b : p.Sk);
+      const long long e = b + p.chunk;
+      kend = (int)(e < p.Sk ? e : p.Sk);
+    }
+    begin_tile(qt);
+    const int kend_q = min(kend, kend_of(qt));
+    sweep(kbeg, kend_q, kend_q > kbeg ? ceil_div_i(kend_q - kbeg, BN) : 0);
+    write_out();
   } else {
-    // u is stored as (l / c) * sum(rounded p * v): u / l is then the chunk's consistent
-    // weighted average, while u still equals sum(exp(s - m) v) up to rounding.
-    const size_t sidx = size_t(split) * size_t(BH) * p.Sq + ridx;
-    out = p.ws_u + sidx * D;
-    sc = c_tot > 0.0f ? p.v_scale * l_tot / (TR::kPScale * c_tot) : 0.0f;
-    if (g == 0) {
-      p.ws_m[sidx] = l_tot > 0.0f ? m_run * kLn2 : -__builtin_inff();
-      p.ws_l[sidx] = l_tot;
+    // Tiles t (lighter) and T (heavier) of the pair, in key tiles of BN.  When nqt is
+    // odd the middle tile pairs with itself and the two groups just split its sweep.
+    const int t = qt, T = nqt - 1 - qt;
+    const int ke_t = kend_of(t), ke_T = kend_of(T);
+    const int w_t = t < T ? ceil_div_i(ke_t, BN) : 0;
+    const int w_T = ceil_div_i(ke_T, BN);
+    // Phase 1: A sweeps tile t, B the last w_t key tiles of T (both end on their
+    // diagonal).  Phase 2: A takes key tiles [0, x) of T, B takes [x, w_T - w_t).
+    const int mid = w_T - w_t;                  // key tiles of T left after phase 1
+    const int x = mid / 2;
+    if (grp == 0) begin_tile(t < T ? t : T);
+    else begin_tile(T);
+    if (t < T) {
+      if (grp == 0) sweep(0, ke_t, w_t);
+      else sweep(mid * BN, ke_T, w_t);
+      if (grp == 0) {
+        write_out();
+        begin_tile(T);
+      }
+    }
+    // Phase 2 (both groups run mid - x iterations; A's last one may be idle).
+    if (grp == 0) sweep(0, x * BN, mid - x);
+    else sweep(x * BN, t < T ? mid * BN : ke_T, mid - x);
+    // A hands its state of tile T to B through LDS (the rings are drained): the
+    // accumulator block db of lane L of wavefront w goes to ks<db>[(w * 64 + L) * 16],
+    // the running maximum and sums to vs0.
+    static_assert(NDB <= NS, "one ring stage array per accumulator block");
+    static_assert(P::STAGE_K * NG >= kWaves * 64 * 16 * 4, "stage array holds a block");
+    float* hand_m = reinterpret_cast<float*>(vs0);
+    const int slot = wave * 64 + lane;
+    if (grp == 0) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        float* dst = reinterpret_cast<float*>(db == 0 ? ks0 : db == 1 ? ks1 : db == 2 ? ks2 : ks3) + slot * 16;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          f32x4_t v4 = {oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2],
+                        oacc[db][4 * jj + 3]};
+          *reinterpret_cast<f32x4_t*>(dst + 4 * jj) = v4;
+        }
+      }
+      hand_m[slot * 3 + 0] = m_run;
+      hand_m[slot * 3 + 1] = l_run;
+      hand_m[slot * 3 + 2] = c_run;
+    }
+    block_sync();
+    if (grp == 1) {
+      const float ma = hand_m[slot * 3 + 0];
+      const float la = hand_m[slot * 3 + 1];
+      const float ca = hand_m[slot * 3 + 2];
+      const float mn = __builtin_fmaxf(ma, m_run);
+      const float wa = ma == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(ma - mn);
+      const float wb = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const float* src = reinterpret_cast<const float*>(db == 0 ? ks0 : db == 1 ? ks1 : db == 2 ? ks2 : ks3) + slot * 16;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(src + 4 * jj);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[db][4 * jj + e] = wa * v4[e] + wb * oacc[db][4 * jj + e];
+        }
+      }
+      l_run = wa * la + wb * l_run;
+      c_run = wa * ca + wb * c_run;
+      m_run = mn;
+      write_out();
     }
   }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      f32x4_t v4 = {oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2],
-                    oacc[db][4 * jj + 3]};
-      *reinterpret_cast<f32x4_t*>(out + db * 32 + jj * 8 + g * 4) = v4 * sc;
-    }
 }
 
 
@@ -998,11 +1117,19 @@ void attn_merge_kernel(MergeArgs a) {
 template <int DT, int D>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   constexpr int BN = block_n(DT, D);
-  const int64_t nwg = int64_t(a.B) * a.H * ((a.Sq + kBlockM - 1) / kBlockM) * a.num_splits;
+  const int64_t nqt = (a.Sq + kBlockM - 1) / kBlockM;
+  if constexpr (pairs_supported(DT, D)) {
+    if (a.pair_order == 2 && !a.split_mode && a.causal) {
+      const int64_t nwg = int64_t(a.B) * a.H * ((nqt + 1) / 2);
+      hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN, kPairs>), dim3(unsigned(nwg)), dim3(2 * kThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  const int64_t nwg = int64_t(a.B) * a.H * nqt * a.num_splits;
   if (a.split_mode)
-    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN, true>), dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN, kSplit>), dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN, false>), dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN, kPlain>), dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1051,7 +1178,9 @@ int device_cu_count() {
   return n;
 }
 
-const char* fwd_kernel_name(int dtype, int d, int split_mode) {
+const char* fwd_kernel_name(int dtype, int d, int split_mode, int pairs) {
+  if (pairs && pairs_supported(dtype, d))
+    return d == 64 ? "attn_fwd_causal_pairs_bf16_d64_bm256_bn64" : "attn_fwd_causal_pairs_bf16_d128_bm256_bn32";
   static const char* names[3][3][2] = {
       {{"attn_fwd_f32_d64_bm128_bn32", "attn_fwd_splitkv_f32_d64_bm128_bn32"},
        {"attn_fwd_f32_d128_bm128_bn32", "attn_fwd_splitkv_f32_d128_bm128_bn32"},
