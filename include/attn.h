@@ -134,10 +134,11 @@ attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o
 
 /*
  * Launch plan queries.  num_splits = 0 describes attn_fwd; num_splits >= 1 describes
- * attn_fwd_splitkv with that many chunks.  Every call launches one four-wavefront
- * workgroup per 128 query rows (times num_splits); for causal attn_fwd calls the order
- * of the query tiles over the grid depends on the current device's CU count (a HIP
- * query), the grid size does not.
+ * attn_fwd_splitkv with that many chunks.  A call launches one four-wavefront workgroup
+ * per 128 query rows (times num_splits), except causal bf16 calls with d <= 128 whose
+ * tile pairs fit one workgroup per CU: those launch one eight-wavefront workgroup per
+ * pair of 128-row tiles (t, last - t), 256 query rows.  Causal plans depend on the
+ * current device's CU count (a HIP query).
  */
 /* Query rows per workgroup, or 0 if an argument is out of range. */
 int attn_block_m(int B, int H, int Sq, int d, int causal, attn_dtype dtype, int num_splits);

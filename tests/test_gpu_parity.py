@@ -230,6 +230,41 @@ def test_splitkv_counts_with_empty_chunks(dtype, causal):
         check(f"split {dtype} causal={causal} n={n}", o, lse, ro, rl, dtype)
 
 
+# ------------------------------------------------------------------ causal schedules
+def test_causal_tile_pairs_plan_and_parity():
+    """A causal bf16 grid whose tile pairs fit one workgroup per CU runs the pair kernel
+    (two groups per workgroup split each pair's keys and merge); odd tile count (the
+    middle tile pairs with itself), Sq != Sk, ragged last tile."""
+    B, H, Sq, Sk, d = 1, 3, 1100, 1500, 128
+    nqt = -(-Sq // 128)
+    assert ea.attn_kernel_name(B, H, Sq, d, 1, ea.ATTN_BF16).startswith("attn_fwd_causal_pairs_bf16_d128")
+    assert ea.attn_block_m(B, H, Sq, d, 1, ea.ATTN_BF16) == 256
+    assert ea.attn_num_workgroups(B, H, Sq, d, 1, ea.ATTN_BF16) == B * H * ((nqt + 1) // 2)
+    inp = si.make_attention_inputs(B, H, Sq, Sk, d, seed=21, dtype="bf16", hot_row_frac=0.01)
+    sc = scale_for(d)
+    o, lse = _run_fwd(inp, sc, True)
+    ro, rl = oracle.attention(inp.q64, inp.k64, inp.v64, sc, True)
+    check("causal pairs bf16 (1, 3, 1100, 1500)", o, lse, ro, rl, "bf16")
+
+
+def test_causal_schedules_without_pairs():
+    """fp8 (no pair kernel): complementary tiles per CU when the grid is resident at
+    once; bf16 with a grid larger than one workgroup per CU: longest sweeps first."""
+    for (B, H, S, d, dtype, seed) in ((1, 2, 700, 64, "fp8", 22), (4, 40, 700, 64, "bf16", 23)):
+        adt = ea.ATTN_FP8_E4M3 if dtype == "fp8" else ea.ATTN_BF16
+        assert not ea.attn_kernel_name(B, H, S, d, 1, adt).startswith("attn_fwd_causal_pairs")
+        assert ea.attn_num_workgroups(B, H, S, d, 1, adt) == B * H * -(-S // 128)
+        inp = si.make_attention_inputs(B, H, S, S, d, seed=seed, dtype=dtype)
+        sc = scale_for(d)
+        o, lse = _run_fwd(inp, sc, True)
+        rows = sample_rows(S, 64, seed)
+        heads = [0, B * H // 2, B * H - 1]
+        ro, rl = oracle_rows(inp, sc, True, rows=rows, heads=heads)
+        og = o.reshape(B * H, S, d)[heads][:, rows]
+        lg = lse.reshape(B * H, S)[heads][:, rows]
+        check(f"causal {dtype} {(B, H, S, d)}", og, lg, ro, rl, dtype)
+
+
 # ------------------------------------------------------------------ hygiene
 def test_repeat_runs_are_bitwise_identical():
     inp = si.make_attention_inputs(2, 4, 700, 700, 128, seed=11, dtype="bf16")
