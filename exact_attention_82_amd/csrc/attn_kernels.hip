@@ -1019,19 +1019,28 @@ void attn_fwd_kernel(FwdArgs p) {
     // diagonal).  Phase 2: A takes key tiles [0, x) of T, B takes [x, w_T - w_t).
     const int mid = w_T - w_t;                  // key tiles of T left after phase 1
     const int x = mid / 2;
-    if (grp == 0) begin_tile(t < T ? t : T);
-    else begin_tile(T);
-    if (t < T) {
-      if (grp == 0) sweep(0, ke_t, w_t);
-      else sweep(mid * BN, ke_T, w_t);
-      if (grp == 0) {
+    begin_tile(grp == 0 && t < T ? t : T);
+    // One sweep call site for both groups and both phases keeps a single copy of the
+    // sweep's code, which both groups execute (instruction-cache footprint).
+#pragma nounroll
+    for (int ph = t < T ? 0 : 1; ph < 2; ++ph) {
+      int kb, ke, n;
+      if (ph == 0) {
+        kb = grp == 0 ? 0 : mid * BN;
+        ke = grp == 0 ? ke_t : ke_T;
+        n = w_t;
+      } else {
+        // both groups run mid - x iterations; A's last one may be idle
+        kb = grp == 0 ? 0 : x * BN;
+        ke = grp == 0 ? x * BN : (t < T ? mid * BN : ke_T);
+        n = mid - x;
+      }
+      sweep(kb, ke, n);
+      if (ph == 0 && grp == 0) {
         write_out();
         begin_tile(T);
       }
     }
-    // Phase 2 (both groups run mid - x iterations; A's last one may be idle).
-    if (grp == 0) sweep(0, x * BN, mid - x);
-    else sweep(x * BN, t < T ? mid * BN : ke_T, mid - x);
     // A hands its state of tile T to B through LDS (the rings are drained): the
     // accumulator block db of lane L of wavefront w goes to ks<db>[(w * 64 + L) * 16],
     // the running maximum and sums to vs0.
