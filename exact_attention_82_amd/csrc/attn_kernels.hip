@@ -1091,36 +1091,63 @@ void attn_fwd_kernel(FwdArgs p) {
 
 
 // ------------------------------------------------------------------ merge kernel
-// One group of D/4 lanes per row, each lane owning 4 consecutive columns.
+// One workgroup of 256 threads per row.  Thread t owns the 16-byte column chunk t % CH
+// (CH = D/4 chunks per row) for the splits s = t / CH, t / CH + NG, ... (NG = 256 / CH
+// split groups), so the n chunk states are read with n / NG independent loads per
+// thread; the group partial sums are then added in LDS in a fixed order (the result
+// does not depend on timing).
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void attn_merge_kernel(MergeArgs a) {
-  constexpr int TPR = D / 4;             // threads per row
-  constexpr int RPB = 256 / TPR;         // rows per block
-  const int64_t row = int64_t(blockIdx.x) * RPB + threadIdx.x / TPR;
-  const int col = (threadIdx.x % TPR) * 4;
-  if (row >= a.rows) return;
-  float M = -__builtin_inff();
-  for (int s = 0; s < a.num_splits; ++s) {
-    const float m = a.ws_m[int64_t(s) * a.rows + row];
-    M = M > m ? M : m;
-  }
-  float L = 0.0f;
-  f32x4_t U = {0.f, 0.f, 0.f, 0.f};
-  if (M != -__builtin_inff()) {
-    for (int s = 0; s < a.num_splits; ++s) {
-      const int64_t i = int64_t(s) * a.rows + row;
-      const float m = a.ws_m[i];
-      if (m == -__builtin_inff()) continue;
-      const float w = expf(m - M);
-      L += w * a.ws_l[i];
-      U += w * *reinterpret_cast<const f32x4_t*>(a.ws_u + i * D + col);
+  constexpr int CH = D / 4;
+  constexpr int NG = 256 / CH;
+  __shared__ f32x4_t part_u[NG][CH];
+  __shared__ float part_l[NG];
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int ch = tid % CH, grp = tid / CH;
+  const int n = a.num_splits;
+  // grid-stride over rows (the grid is capped); the loop bound is uniform per workgroup
+  for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    // global maximum of the chunk maxima (natural-log units; -inf for empty chunks)
+    float M = -__builtin_inff();
+    for (int s = tid; s < n; s += 256) M = __builtin_fmaxf(M, a.ws_m[int64_t(s) * a.rows + row]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, o, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = M;
+    __syncthreads();
+    M = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+
+    float L = 0.0f;
+    f32x4_t U = {0.f, 0.f, 0.f, 0.f};
+    if (M != -__builtin_inff()) {
+      for (int s = grp; s < n; s += NG) {
+        const int64_t i = int64_t(s) * a.rows + row;
+        const float m = a.ws_m[i];
+        if (m == -__builtin_inff()) continue;
+        const float w = expf(m - M);
+        L += w * a.ws_l[i];
+        U += w * *reinterpret_cast<const f32x4_t*>(a.ws_u + i * D + ch * 4);
+      }
     }
+    part_u[grp][ch] = U;
+    if (ch == 0) part_l[grp] = L;
+    __syncthreads();
+    if (grp == 0) {
+      U = part_u[0][ch];
+      L = part_l[0];
+#pragma unroll
+      for (int gi = 1; gi < NG; ++gi) {
+        U += part_u[gi][ch];
+        L += part_l[gi];
+      }
+      const bool empty = !(L > 0.0f);
+      const float inv = empty ? 0.0f : 1.0f / L;
+      *reinterpret_cast<f32x4_t*>(a.o + row * D + ch * 4) = U * inv;
+      if (ch == 0) a.lse[row] = empty ? -__builtin_inff() : M + logf(L);
+    }
+    __syncthreads();  // part_u / part_l / red are reused by the next row
   }
-  const bool empty = !(L > 0.0f);
-  const float inv = empty ? 0.0f : 1.0f / L;
-  *reinterpret_cast<f32x4_t*>(a.o + row * D + col) = U * inv;
-  if (col == 0) a.lse[row] = empty ? -__builtin_inff() : M + logf(L);
 }
 
 template <int DT, int D>
@@ -1166,11 +1193,11 @@ int launch_fwd(const FwdArgs& a, void* stream) {
 
 int launch_merge(const MergeArgs& a, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  auto blocks = [&](int d) { return unsigned((a.rows + (256 / (d / 4)) - 1) / (256 / (d / 4))); };
+  const dim3 grid(unsigned(a.rows < (int64_t(1) << 20) ? a.rows : (int64_t(1) << 20)));
   switch (a.d) {
-    case 64: hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks(64)), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks(128)), dim3(256), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(attn_merge_kernel<256>, dim3(blocks(256)), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(attn_merge_kernel<256>, grid, dim3(256), 0, s, a); break;
     default: return int(hipErrorInvalidValue);
   }
   return int(hipGetLastError());
