@@ -558,6 +558,73 @@ __device__ __forceinline__ void softmax_sums(const f32x16_t (&s)[BN / 32], const
   }
 }
 
+// Main-loop variant for bf16 without a per-tile row maximum.  The probabilities are
+// taken against the running reference m_run as it stands, and their exact sum tells
+// whether that was safe: the sum stays <= 2^kSumCap unless some score exceeds the
+// reference by about kSumCap (log2 units) or there is no reference yet (m_run = -inf
+// gives +inf).  Only then (rare: a new score far above everything seen so far) is the
+// tile redone the exact way: row maximum, new reference, correction of the
+// accumulator and the running sums.  The result is the same exact softmax; the
+// unnormalised probabilities are just allowed to reach 2^kSumCap instead of 2^kTau.
+constexpr float kSumCap = 4294967296.0f;  // 2^32
+
+template <int BN>
+__device__ __forceinline__ float softmax_exp_ref(const f32x16_t (&s)[BN / 32], f32x16_t (&p)[BN / 32],
+                                                 float m_ref, float sl2) {
+  float ls = 0.0f;
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      p[b][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][j], sl2, -m_ref));
+      ls += p[b][j];
+    }
+  return ls;
+}
+
+template <int BN, int NDB>
+__device__ __forceinline__ float softmax_redo(const f32x16_t (&s)[BN / 32], f32x16_t (&p)[BN / 32],
+                                              f32x16_t (&oacc)[NDB], float& m_run, float& l_run,
+                                              float& c_run, float sl2) {
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, s[b][j]);
+  const float m_new = __builtin_fmaxf(m_run, pair_max(mx) * sl2);
+  if (m_new != -__builtin_inff()) {
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+    l_run *= alpha;
+    c_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
+    m_run = m_new;
+  }
+  return softmax_exp_ref<BN>(s, p, m_run == -__builtin_inff() ? 0.0f : m_run, sl2);
+}
+
+// Probabilities -> value-MFMA operands (bf16), and the sum of exactly those values.
+template <int BN>
+__device__ __forceinline__ float pack_bf16(const f32x16_t (&p)[BN / 32], PTile<DT_BF16, BN>& pt) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float cs = 0.0f;
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x8_t x = {p[b][8 * h + 0], p[b][8 * h + 1], p[b][8 * h + 2], p[b][8 * h + 3],
+                   p[b][8 * h + 4], p[b][8 * h + 5], p[b][8 * h + 6], p[b][8 * h + 7]};
+      pt.pk[b][h] = __builtin_convertvector(x, bf16x8_t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2_t two = {pt.pk[b][h][2 * e], pt.pk[b][h][2 * e + 1]};
+        cs = __builtin_amdgcn_fdot2_f32_bf16(two, ones, cs, false);
+      }
+    }
+  return cs;
+}
+
 template <int DT, int BN, int NDB>
 __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], PTile<DT, BN>& pt,
                                              f32x16_t (&oacc)[NDB], float& m_run, float& l_run,
@@ -667,6 +734,25 @@ __device__ __forceinline__ void interleave_step() {
   constexpr int VE = NKB * (32 + 8);          // fma + exp per score, one convert per pair
   constexpr int VS = NKB * (16 + 8);          // exact sum, consistent sum
   sched_pairs<NQ, 0x8, 1, 0x2, (VE + NQ - 1) / NQ>();
+  sched_pairs<NP, 0x8, 1, 0x2, (VS + NP - 1) / NP>();
+}
+
+// The same for the bf16 main loop without a row maximum, whose tile step has two
+// scheduling regions (before and after the rare re-reference branch): the S^T MFMAs of
+// the next tile with the exponentials and the exact sum, then the value MFMAs with the
+// conversion and the consistent sum.
+template <int D, int BN>
+__device__ __forceinline__ void interleave_exp() {
+  constexpr int NKB = BN / 32;
+  constexpr int NQ = (D / 16) * NKB;
+  constexpr int VE = NKB * 48;                // fma + exp + add per score
+  sched_pairs<NQ, 0x8, 1, 0x2, (VE + NQ - 1) / NQ>();
+}
+template <int D, int BN>
+__device__ __forceinline__ void interleave_pv() {
+  constexpr int NKB = BN / 32;
+  constexpr int NP = NKB * 2 * (D / 32);
+  constexpr int VS = NKB * 16;                // converts and dot products
   sched_pairs<NP, 0x8, 1, 0x2, (VS + NP - 1) / NP>();
 }
 
@@ -886,12 +972,16 @@ void attn_fwd_kernel(FwdArgs p) {
         VOps<DT, D, BN> vo;
         load_kops<DT, D, BN>(ko, kb, pipe.ln);
         load_vops<DT, D, BN>(vo, vb, pipe.ln);
-        const float ms = softmax_rescale<DT, BN, NDB>(s_cur, oacc, m_run, l_run, c_run, sl2);
         qk_regs<DT, D, BN>(s_next, ko, qop);
-        softmax_exp<DT, BN>(s_cur, pt, ms, sl2);
+        f32x16_t pr[NKB];
+        float ls = softmax_exp_ref<BN>(s_cur, pr, m_run, sl2);
+        interleave_exp<D, BN>();
+        if (__builtin_amdgcn_ballot_w64(!(ls <= kSumCap)))
+          ls = softmax_redo<BN, NDB>(s_cur, pr, oacc, m_run, l_run, c_run, sl2);
+        l_run += ls;
+        c_run += pack_bf16<BN>(pr, pt);
         pv_regs<DT, D, BN>(oacc, pt, vo);
-        softmax_sums<DT, BN>(s_cur, pt, l_run, c_run);
-        interleave_step<DT, D, BN>();
+        interleave_pv<D, BN>();
       } else {
         pipe.qk(s_next, kb, qop);
         softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
