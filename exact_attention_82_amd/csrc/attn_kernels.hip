@@ -1105,8 +1105,10 @@ void attn_fwd_kernel(FwdArgs p) {
     const int ke_t = kend_of(t), ke_T = kend_of(T);
     const int w_t = t < T ? ceil_div_i(ke_t, BN) : 0;
     const int w_T = ceil_div_i(ke_T, BN);
-    // Phase 1: A sweeps tile t, B the last w_t key tiles of T (both end on their
-    // diagonal).  Phase 2: A takes key tiles [0, x) of T, B takes [x, w_T - w_t).
+    // Phase 1: A sweeps tile t, B the first w_t key tiles of T, so that both groups,
+    // and all workgroups of the head, stream the keys from 0 in step (one pass through
+    // the XCD's L2).  Phase 2: A takes key tiles [w_t, w_t + x) of T and B takes the
+    // rest, [w_t + x, w_T), ending on T's diagonal.
     const int mid = w_T - w_t;                  // key tiles of T left after phase 1
     const int x = mid / 2;
     begin_tile(grp == 0 && t < T ? t : T);
@@ -1116,13 +1118,13 @@ void attn_fwd_kernel(FwdArgs p) {
     for (int ph = t < T ? 0 : 1; ph < 2; ++ph) {
       int kb, ke, n;
       if (ph == 0) {
-        kb = grp == 0 ? 0 : mid * BN;
-        ke = grp == 0 ? ke_t : ke_T;
+        kb = 0;
+        ke = grp == 0 ? ke_t : min(w_t * BN, ke_T);
         n = w_t;
       } else {
         // both groups run mid - x iterations; A's last one may be idle
-        kb = grp == 0 ? 0 : x * BN;
-        ke = grp == 0 ? x * BN : (t < T ? mid * BN : ke_T);
+        kb = (grp == 0 ? w_t : w_t + x) * BN;
+        ke = grp == 0 ? (w_t + x) * BN : ke_T;
         n = mid - x;
       }
       sweep(kb, ke, n);
