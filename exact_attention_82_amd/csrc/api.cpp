@@ -38,9 +38,16 @@ attn_status check_shape(int B, int H, int Sq, int Sk, int d, int dtype) {
   return ATTN_OK;
 }
 
-// Kernel plan of attn_fwd; only causal plans depend on the device (its CU count).
+// Kernel plan of attn_fwd; it depends on the device's CU count (a cached HIP query).
 attn::FwdPlan plan_for(int B, int H, int Sq, int d, int causal, int dtype) {
-  return attn::plan_fwd(B, H, Sq, d, causal, dtype, causal ? attn::device_cu_count() : 0);
+  return attn::plan_fwd(B, H, Sq, d, causal, dtype, attn::device_cu_count());
+}
+
+// Schedule of attn_fwd_splitkv: the two-group kernel when the grid has at most one
+// workgroup per CU.
+int splitkv_schedule(int B, int H, int Sq, int d, int dtype, int num_splits) {
+  const long long nwg = (long long)B * H * ((Sq + attn::kBlockM - 1) / attn::kBlockM) * num_splits;
+  return attn::dual_schedule(nwg, dtype, d, attn::device_cu_count());
 }
 
 attn_status launched(int hip_err) {
@@ -121,7 +128,7 @@ attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v,
   a.split_mode = 1;
   a.scale_log2 = sl2;
   a.v_scale = v_descale;
-  a.pair_order = 0;
+  a.pair_order = splitkv_schedule(B, H, Sq, d, dtype, num_splits);
   a.head_group = attn::head_group(int64_t(B) * H, int((Sq + attn::kBlockM - 1) / attn::kBlockM));
   return launched(attn::launch_fwd(a, stream));
 }
@@ -171,8 +178,9 @@ int64_t attn_num_workgroups(int B, int H, int Sq, int d, int causal, attn_dtype 
 const char* attn_kernel_name(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
                              int num_splits) {
   if (attn_block_m(B, H, Sq, d, causal, dtype, num_splits) == 0) return "unsupported";
-  if (num_splits >= 1) return attn::fwd_kernel_name(dtype, d, 1, 0);
-  return attn::fwd_kernel_name(dtype, d, 0, plan_for(B, H, Sq, d, causal, dtype).pair_order == 2);
+  if (num_splits >= 1)
+    return attn::fwd_kernel_name(dtype, d, 1, splitkv_schedule(B, H, Sq, d, dtype, num_splits));
+  return attn::fwd_kernel_name(dtype, d, 0, plan_for(B, H, Sq, d, causal, dtype).pair_order);
 }
 
 const char* attn_status_string(attn_status s) {

@@ -36,8 +36,9 @@ struct FwdArgs {
   int split_mode; // 0: O and lse; 1: workspace states
   float scale_log2;  // scale * q_descale * k_descale * log2(e)
   float v_scale;     // v_descale
-  int pair_order;    // causal schedule: 0 longest first, 1 complementary tiles per CU,
-                     // 2 pairs of tiles shared by the two groups of one workgroup
+  int pair_order;    // schedule: 0 causal longest first / plain, 1 complementary causal
+                     // tiles per CU, 2 causal tile pairs shared by the two groups of one
+                     // workgroup, 3 two groups splitting each tile's keys (small grids)
   int head_group;    // heads whose query tiles are scheduled together (divides B*H)
 };
 
@@ -52,6 +53,15 @@ struct FwdPlan {
 // query tiles) exists for bf16 with d <= 128: two rings of 64 KiB fit in the LDS.
 constexpr bool pairs_supported(int dtype, int d) { return dtype == 1 && d <= 128; }
 
+// The two-group kernel that splits each tile's keys: bf16 with d <= 128 and fp8 with
+// d = 128 (the LDS hand-off at the end needs 16 KiB ring stages).
+constexpr bool dual_supported(int dtype, int d) {
+  return (dtype == 1 && d <= 128) || (dtype == 2 && d == 128);
+}
+inline int dual_schedule(long long nwg, int dtype, int d, int cus) {
+  return (dual_supported(dtype, d) && cus > 0 && nwg <= cus) ? 3 : 0;
+}
+
 // head_group: the largest power of two dividing B*H whose query tiles (head_group *
 // ceil(Sq / 128) workgroups) fit in one XCD's resident set of 64 workgroups, so that
 // those workgroups share the heads' key/value tiles in the XCD's L2.
@@ -64,21 +74,24 @@ inline int head_group(long long bh, int nqt) {
 // Causal sweeps differ in length by up to nqt times.  In order of preference:
 //   2: one workgroup per pair of tiles (t, nqt-1-t) whose two groups split the pair's
 //      keys evenly, when one such workgroup per CU covers the grid;
+//   3: (causal or not) two groups per workgroup splitting each tile's keys, when the
+//      grid has at most one workgroup per CU (a second wavefront per SIMD);
 //   1: workgroups i and i + grid/2, which share a CU when the whole grid is resident
 //      (at most `per_cu` per CU), get complementary tiles t and nqt-1-t;
-//   0: longest sweeps first.
+//   0: longest sweeps first (causal), or the plain order.
 inline FwdPlan plan_fwd(int B, int H, int Sq, int d, int causal, int dtype, int cus) {
   const long long bh = (long long)B * H;
   const long long nqt = (Sq + kBlockM - 1) / kBlockM;
   FwdPlan pl{kBlockM, 0, head_group(bh, (int)nqt)};
-  if (causal && cus > 0) {
+  if (causal && cus > 0 && pairs_supported(dtype, d) && bh * ((nqt + 1) / 2) <= cus) {
+    pl.pair_order = 2;
+    pl.block_m = 2 * kBlockM;
+    return pl;
+  }
+  pl.pair_order = dual_schedule(bh * nqt, dtype, d, cus);
+  if (pl.pair_order == 0 && causal && cus > 0) {
     const int per_cu = (d >= 256 || dtype == 0) ? 1 : 2;
-    if (pairs_supported(dtype, d) && bh * ((nqt + 1) / 2) <= cus) {
-      pl.pair_order = 2;
-      pl.block_m = 2 * kBlockM;
-    } else if (bh * nqt <= (long long)cus * per_cu) {
-      pl.pair_order = 1;
-    }
+    if (bh * nqt <= (long long)cus * per_cu) pl.pair_order = 1;
   }
   return pl;
 }
@@ -114,6 +127,6 @@ int launch_fwd(const FwdArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 // Compute units of the current device (cached per device), or 0 if unknown.
 int device_cu_count();
-const char* fwd_kernel_name(int dtype, int d, int split_mode, int pairs);
+const char* fwd_kernel_name(int dtype, int d, int split_mode, int sched);
 
 }  // namespace attn

@@ -767,18 +767,22 @@ __device__ __forceinline__ void interleave_pv() {
 //   B merges the two (the split-K merge of the pages, inside one workgroup).  Every CU
 //   then does the same work with both groups busy to the end, where separate
 //   workgroups of very different lengths would leave one alone on its CU.
-enum : int { kPlain = 0, kSplit = 1, kPairs = 2 };
+// MODE kDualPlain / kDualSplit: as kPlain / kSplit, but two four-wavefront groups split
+//   the tile's key range in halves and merge the same way (used when the grid has at
+//   most one workgroup per CU: the second group gives every SIMD a second wavefront).
+enum : int { kPlain = 0, kSplit = 1, kPairs = 2, kDualPlain = 3, kDualSplit = 4 };
+constexpr bool two_groups(int mode) { return mode == kPairs || mode == kDualPlain || mode == kDualSplit; }
 
 template <int DT, int D, int BN, int MODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads * (MODE == kPairs ? 2 : 1),
-                                                      kThreads * (MODE == kPairs ? 2 : 1)),
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads * (two_groups(MODE) ? 2 : 1),
+                                                      kThreads * (two_groups(MODE) ? 2 : 1)),
                           amdgpu_waves_per_eu(waves_per_eu(DT, D), waves_per_eu(DT, D))))
 void attn_fwd_kernel(FwdArgs p) {
   using TR = Traits<DT>;
   using P = Pipe<DT, D, BN, kWaves>;
   using Op = typename TR::Op;
-  constexpr bool SPLIT = MODE == kSplit;
-  constexpr int NG = MODE == kPairs ? 2 : 1;  // four-wavefront groups per workgroup
+  constexpr bool SPLIT = MODE == kSplit || MODE == kDualSplit;
+  constexpr int NG = two_groups(MODE) ? 2 : 1;  // four-wavefront groups per workgroup
   constexpr int EB = TR::kBytes;
   constexpr int KSTEPS = D / TR::kKS;  // MFMAs over d per 32-key block of S^T
   constexpr int NKB = BN / 32;         // 32-key blocks per tile
@@ -800,7 +804,7 @@ void attn_fwd_kernel(FwdArgs p) {
     // batch*head fastest: all pairs of a head land on one XCD (index mod 8).
     bh = blockIdx.x % BH;
     qt = blockIdx.x / BH;              // the lighter tile t of the pair
-  } else if (!SPLIT && p.causal && p.pair_order) {
+  } else if (!SPLIT && p.causal && p.pair_order == 1) {
     // The whole grid is resident at once (two workgroups per CU, dispatched in index
     // order): workgroups i and i + grid/2 share a CU, so they get complementary query
     // tiles (t and nqt-1-t) of the same head and every CU gets the same work.
@@ -1086,19 +1090,30 @@ void attn_fwd_kernel(FwdArgs p) {
       }
   };
 
-  if constexpr (MODE != kPairs) {
-    int kbeg = 0, kend = p.Sk;
-    if (SPLIT) {
-      const long long b = (long long)split * p.chunk;
-      kbeg = (int)(b < p.Sk ? b : p.Sk);
-      const long long e = b + p.chunk;
-      kend = (int)(e < p.Sk ? e : p.Sk);
-    }
+  // keys of this workgroup's (query tile, chunk)
+  int kbeg = 0, kend = p.Sk;
+  if (SPLIT) {
+    const long long b = (long long)split * p.chunk;
+    kbeg = (int)(b < p.Sk ? b : p.Sk);
+    const long long e = b + p.chunk;
+    kend = (int)(e < p.Sk ? e : p.Sk);
+  }
+  if constexpr (NG == 1) {
     begin_tile(qt);
     const int kend_q = min(kend, kend_of(qt));
     sweep(kbeg, kend_q, kend_q > kbeg ? ceil_div_i(kend_q - kbeg, BN) : 0);
     write_out();
   } else {
+    if constexpr (MODE != kPairs) {
+      // Dual: group A takes the first half of the key tiles, B the rest (B's extra
+      // iteration, if any, is idle); both end with a partial state of the same tile.
+      begin_tile(qt);
+      const int kend_q = min(kend, kend_of(qt));
+      const int nt = kend_q > kbeg ? ceil_div_i(kend_q - kbeg, BN) : 0;
+      const int half = (nt + 1) / 2;
+      const int cut = min(kend_q, kbeg + half * BN);
+      sweep(grp == 0 ? kbeg : cut, grp == 0 ? cut : kend_q, half);
+    } else {
     // Tiles t (lighter) and T (heavier) of the pair, in key tiles of BN.  When nqt is
     // odd the middle tile pairs with itself and the two groups just split its sweep.
     const int t = qt, T = nqt - 1 - qt;
@@ -1133,7 +1148,8 @@ void attn_fwd_kernel(FwdArgs p) {
         begin_tile(T);
       }
     }
-    // A hands its state of tile T to B through LDS (the rings are drained): the
+    }
+    // A hands its state of the shared tile to B through LDS (the rings are drained): the
     // accumulator block db of lane L of wavefront w goes to ks<db>[(w * 64 + L) * 16],
     // the running maximum and sums to vs0.
     static_assert(NDB <= NS, "one ring stage array per accumulator block");
@@ -1254,6 +1270,15 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
     }
   }
   const int64_t nwg = int64_t(a.B) * a.H * nqt * a.num_splits;
+  if constexpr (dual_supported(DT, D)) {
+    if (a.pair_order == 3) {
+      if (a.split_mode)
+        hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN, kDualSplit>), dim3(unsigned(nwg)), dim3(2 * kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN, kDualPlain>), dim3(unsigned(nwg)), dim3(2 * kThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (a.split_mode)
     hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN, kSplit>), dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
   else
@@ -1306,9 +1331,16 @@ int device_cu_count() {
   return n;
 }
 
-const char* fwd_kernel_name(int dtype, int d, int split_mode, int pairs) {
-  if (pairs && pairs_supported(dtype, d))
+const char* fwd_kernel_name(int dtype, int d, int split_mode, int sched) {
+  if (sched == 2 && pairs_supported(dtype, d))
     return d == 64 ? "attn_fwd_causal_pairs_bf16_d64_bm256_bn64" : "attn_fwd_causal_pairs_bf16_d128_bm256_bn32";
+  if (sched == 3 && dual_supported(dtype, d)) {
+    if (dtype == DT_FP8)
+      return split_mode ? "attn_fwd_splitkv_dual_fp8_d128_bm128_bn64" : "attn_fwd_dual_fp8_d128_bm128_bn64";
+    if (d == 64)
+      return split_mode ? "attn_fwd_splitkv_dual_bf16_d64_bm128_bn64" : "attn_fwd_dual_bf16_d64_bm128_bn64";
+    return split_mode ? "attn_fwd_splitkv_dual_bf16_d128_bm128_bn32" : "attn_fwd_dual_bf16_d128_bm128_bn32";
+  }
   static const char* names[3][3][2] = {
       {{"attn_fwd_f32_d64_bm128_bn32", "attn_fwd_splitkv_f32_d64_bm128_bn32"},
        {"attn_fwd_f32_d128_bm128_bn32", "attn_fwd_splitkv_f32_d128_bm128_bn32"},
