@@ -247,6 +247,21 @@ def test_causal_tile_pairs_plan_and_parity():
     check("causal pairs bf16 (1, 3, 1100, 1500)", o, lse, ro, rl, "bf16")
 
 
+def test_small_grids_run_two_groups_per_workgroup():
+    """Grids of at most one workgroup per CU split each tile's keys between two groups
+    (the split-KV chunks too); parity of those kernels is covered by every small-shape
+    test above, this pins the choice."""
+    assert ea.attn_kernel_name(1, 2, 300, 128, 0, ea.ATTN_BF16).startswith("attn_fwd_dual_bf16_d128")
+    assert ea.attn_kernel_name(1, 8, 128, 128, 0, ea.ATTN_FP8_E4M3, 16).startswith("attn_fwd_splitkv_dual_fp8_d128")
+    assert ea.attn_kernel_name(1, 8, 8192, 128, 0, ea.ATTN_BF16) == "attn_fwd_bf16_d128_bm128_bn32"
+    inp = si.make_attention_inputs(1, 2, 300, 333, 128, seed=24, dtype="bf16", hot_row_frac=0.02)
+    sc = scale_for(128)
+    for causal in (False, True):
+        o, lse = _run_fwd(inp, sc, causal)
+        ro, rl = oracle.attention(inp.q64, inp.k64, inp.v64, sc, causal)
+        check(f"two groups bf16 causal={causal}", o, lse, ro, rl, "bf16")
+
+
 def test_causal_schedules_without_pairs():
     """fp8 (no pair kernel): complementary tiles per CU when the grid is resident at
     once; bf16 with a grid larger than one workgroup per CU: longest sweeps first."""
