@@ -1,0 +1,69 @@
+"""Launch-plan logic of attn_fwd (host code in attn_internal.h), compiled with the host
+C++ compiler and run on the CPU: which schedule each shape gets for a given CU count."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+BF16, FP8, F32 = 1, 2, 0
+
+
+@pytest.fixture(scope="module")
+def probe(tmp_path_factory):
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    exe = str(tmp_path_factory.mktemp("plan") / "plan_probe")
+    subprocess.run([cxx, "-std=c++17", "-O1", os.path.join(HERE, "plan_probe.cpp"), "-o", exe], check=True)
+
+    def run(cases):
+        text = "".join(" ".join(str(x) for x in c) + "\n" for c in cases)
+        out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True).stdout
+        return [tuple(int(v) for v in line.split()) for line in out.strip().splitlines()]
+    return run
+
+
+def test_long_sequence_workload(probe):
+    # B=1, H=8, S=8192, d=128 on 256 CUs: 512 plain workgroups; causal -> 256 tile pairs
+    nc, c = probe([(1, 8, 8192, 128, 0, BF16, 256), (1, 8, 8192, 128, 1, BF16, 256)])
+    assert nc == (128, 0, 1)
+    assert c == (256, 2, 1)
+
+
+def test_many_heads_workload(probe):
+    # B=8, H=32, S=2048, d=64: 4096 workgroups, 16 query tiles per head, 4 heads per group
+    nc, c = probe([(8, 32, 2048, 64, 0, BF16, 256), (8, 32, 2048, 64, 1, BF16, 256)])
+    assert nc == (128, 0, 4)
+    assert c == (128, 0, 4)   # longest sweeps first: far more workgroups than CUs
+
+
+def test_small_grids_use_two_groups(probe):
+    out = probe([(1, 2, 300, 128, 0, BF16, 256), (1, 8, 128, 128, 0, FP8, 256),
+                 (1, 2, 300, 64, 0, FP8, 256), (1, 2, 300, 128, 0, F32, 256)])
+    assert out[0][1] == 3 and out[1][1] == 3     # bf16 d128, fp8 d128: two groups
+    assert out[2][1] == 0 and out[3][1] == 0     # fp8 d64, fp32: no two-group kernel
+
+
+def test_causal_orders(probe):
+    out = probe([(1, 2, 700, 64, 1, FP8, 256),     # resident grid: complementary tiles
+                 (4, 40, 700, 64, 1, BF16, 256),   # 960 workgroups: longest first
+                 (1, 3, 1100, 128, 1, BF16, 256),  # tile pairs (odd tile count)
+                 (1, 8, 8192, 256, 1, BF16, 256)]) # d = 256: no pair kernel, 1 per CU
+    assert out[0][1] == 1
+    assert out[1][1] == 0
+    assert out[2] == (256, 2, 1)
+    assert out[3][1] == 1
+
+
+def test_without_a_device_query_plans_are_plain(probe):
+    for case in [(1, 8, 8192, 128, 1, BF16, 0), (1, 2, 300, 128, 0, BF16, 0)]:
+        assert probe([case])[0][:2] == (128, 0)
+
+
+def test_head_group_divides_heads_and_fits_an_xcd(probe):
+    for bh, nqt in [(256, 16), (8, 64), (6, 3), (7, 5), (12, 4), (1, 1)]:
+        (_, _, g), = probe([(1, bh, nqt * 128, 64, 0, BF16, 1)])
+        assert bh % g == 0 and (g == 1 or g * nqt <= 64)
+        assert not (bh % (2 * g) == 0 and 2 * g * nqt <= 64)   # largest such power of two
