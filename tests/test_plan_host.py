@@ -50,11 +50,13 @@ def test_causal_orders(probe):
     out = probe([(1, 2, 700, 64, 1, FP8, 256),     # resident grid: complementary tiles
                  (4, 40, 700, 64, 1, BF16, 256),   # 960 workgroups: longest first
                  (1, 3, 1100, 128, 1, BF16, 256),  # tile pairs (odd tile count)
-                 (1, 8, 8192, 256, 1, BF16, 256)]) # d = 256: no pair kernel, 1 per CU
+                 (1, 4, 8192, 256, 1, BF16, 256),  # d = 256: no pair kernel; 1 per CU fits
+                 (1, 8, 8192, 256, 1, BF16, 256)]) # ... 2 per CU do not: longest first
     assert out[0][1] == 1
     assert out[1][1] == 0
     assert out[2] == (256, 2, 1)
     assert out[3][1] == 1
+    assert out[4][1] == 0
 
 
 def test_without_a_device_query_plans_are_plain(probe):
