@@ -1027,12 +1027,14 @@ void attn_fwd_kernel(FwdArgs p) {
       // Both loops pass one barrier per tile, so wavefronts may split at different tiles.
       nfull = nfull < 0 ? 0 : (nfull / U) * U;
     }
+    // The full loop runs from tile 0 over a multiple of U tiles, so its unrolled body
+    // needs no per-tile bound check.
     auto run = [&](auto full_c, int t0, int t1) __attribute__((always_inline)) {
       constexpr bool FULL = decltype(full_c)::value;
       for (int t = t0; t < t1; t += U) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-          if (t + j < t1) {
+          if (FULL || t + j < t1) {
             uint8_t* kd = kst(j);
             uint8_t* vd = vst(j + NS - 1);
             const uint8_t* kb = kst(j + 1);
