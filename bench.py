@@ -1,6 +1,8 @@
 """Benchmark of the exact attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+    python bench.py --sweep {c1,c2,c4,c5} > sweep.jsonl     (per-case timing, see below)
+    python bench.py --summarize-sweep sweep.jsonl           (markdown table of those lines)
 
 Workload (default): B=1, H=8, Sq=Sk=8192, d=128, Q/K/V i.i.d. N(0,1) rounded to bf16,
 scale 1/sqrt(d).  One step is one forward pass of the whole path over that batch in
@@ -17,6 +19,15 @@ Prints one JSON line.  Besides the headline throughput it carries
   cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample.
 With the CPU leg, a few sampled rows of two heads are also checked against the oracle's
 outputs (outside the timed region).
+
+--sweep times the other workloads case by case (one JSON line per case and mask): every
+call timed alone with HIP events on its stream after a 512 MiB device read that evicts
+the inputs from L2 and the 256 MB last-level cache, medians over the reps.  c1 (fp32
+B=1,H=2,S=128,d=64) reports microseconds; c2 and the 36 c4 cases (d in 64/128/256, S in
+512/1000/2048, B in 1/8, H=16, bf16 with 1 % of query rows scaled by 30) report TFLOP/s
+against min(bf16 MFMA peak, intensity x 8 TB/s); c5 (fp8 B=1,H=8,Sq=128,Sk=32768,d=128)
+times attn_fwd_splitkv and attn_merge apart for n = 1, 4, 16 and reports the algorithmic
+bytes (Q, K, V read once, O and lse written once) per second against 8 TB/s.
 """
 from __future__ import annotations
 
@@ -167,6 +178,146 @@ def cpu_baseline(inp, scale, budget_s: float, gpu_out):
     return rec, worst
 
 
+def _alg_bytes(B, H, Sq, Sk, d, in_bytes):
+    """Q, K, V read once at their storage width, O and lse (fp32) written once."""
+    return (B * H * Sq * d + 2 * B * H * Sk * d) * in_bytes + B * H * Sq * (d + 1) * 4
+
+
+def _timed_calls(fn, reps, flush):
+    """Per-call HIP-event durations (us) on the current stream, each call after a cache
+    flush outside the event window: a read of a 512 MiB buffer, which leaves the caches
+    full of clean lines (a write would leave dirty lines whose write-back lands inside
+    the next timed call)."""
+    import torch
+    out = []
+    for _ in range(reps):
+        flush.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3)
+    return np.array(out)
+
+
+def _stats(us):
+    return {"median_us": round(float(np.median(us)), 2), "p10_us": round(float(np.percentile(us, 10)), 2),
+            "p90_us": round(float(np.percentile(us, 90)), 2), "min_us": round(float(us.min()), 2)}
+
+
+def sweep(name: str, reps: int, warmup: int):
+    """Per-case timing of the parity workloads; prints one JSON line per case."""
+    import torch
+    import exact_attention_82_amd as ea
+    import synthetic_inputs as si
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB
+
+    def to_dev(inp):
+        if inp.dtype == "bf16":
+            return tuple(torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).to(dev)
+                         for t in (inp.q, inp.k, inp.v))
+        return tuple(torch.from_numpy(np.ascontiguousarray(t)).to(dev) for t in (inp.q, inp.k, inp.v))
+
+    def emit(rec):
+        print(json.dumps(rec), flush=True)
+
+    if name in ("c1", "c2", "c4"):
+        if name == "c1":
+            cases = [(1, 2, 128, 64, 1, "f32", 0.0)]
+        elif name == "c2":
+            cases = [(8, 32, 2048, 64, 2, "bf16", 0.0)]
+        else:
+            cases = [(B, 16, S, d, 400 + (d // 64) * 100 + S // 100 + B, "bf16", 0.01)
+                     for d in (64, 128, 256) for S in (512, 1000, 2048) for B in (1, 8)]
+        for (B, H, S, d, seed, dt, hot) in cases:
+            inp = si.make_attention_inputs(B, H, S, S, d, seed=seed, dtype=dt, hot_row_frac=hot)
+            q, k, v = to_dev(inp)
+            del inp
+            scale = float(np.float32(1.0 / np.sqrt(d)))
+            o = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+            in_bytes = 4 if dt == "f32" else 2
+            for causal in (False, True):
+                fn = lambda: ea.attn_fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
+                for _ in range(warmup):
+                    fn()
+                torch.cuda.synchronize()
+                us = _timed_calls(fn, reps, flush)
+                fl = 4.0 * B * H * S * S * d / (2.0 if causal else 1.0)
+                ab = _alg_bytes(B, H, S, S, d, in_bytes)
+                rec = {"workload": name, "B": B, "H": H, "Sq": S, "Sk": S, "d": d, "dtype": dt,
+                       "causal": causal, "kernel": ea.attn_kernel_name(B, H, S, d, int(causal),
+                                                                       ea.dtype_code(q)),
+                       "reps": reps, **_stats(us)}
+                if dt != "f32":
+                    tf = fl / (float(np.median(us)) * 1e-6) / 1e12
+                    bound = min(PEAK_BF16_TFLOPS, fl / ab * PEAK_HBM_GBS / 1e3)
+                    rec.update({"tflops": round(tf, 2), "flop_per_byte": round(fl / ab, 1),
+                                "bound_tflops": round(bound, 1),
+                                "bound": "mfma" if bound >= PEAK_BF16_TFLOPS else "hbm",
+                                "pct_of_bound": round(100.0 * tf / bound, 2)})
+                emit(rec)
+            del q, k, v, o, lse
+            torch.cuda.empty_cache()
+        return
+    if name == "c5":
+        B, H, Sq, Sk, d = 1, 8, 128, 32768, 128
+        inp = si.make_attention_inputs(B, H, Sq, Sk, d, seed=5, dtype="fp8")
+        q, k, v = to_dev(inp)
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+        ab = _alg_bytes(B, H, Sq, Sk, d, 1)
+        o = torch.empty((B, H, Sq, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+        for n in (1, 4, 16):
+            ws = torch.empty(ea.attn_splitkv_workspace_bytes(B, H, Sq, d, n), dtype=torch.uint8, device=dev)
+            f1 = lambda: ea.attn_fwd_splitkv(q, k, v, n, scale=scale, descales=inp.scales, ws=ws)
+            f2 = lambda: ea.attn_merge(ws, n, B, H, Sq, d, out=o, lse=lse)
+            for _ in range(warmup):
+                f1()
+                f2()
+            torch.cuda.synchronize()
+            u1 = _timed_calls(f1, reps, flush)
+            u2 = _timed_calls(f2, reps, flush)
+            wsb = n * B * H * Sq * (d + 2) * 4
+            t = float(np.median(u1)) + float(np.median(u2))
+            emit({"workload": "c5", "B": B, "H": H, "Sq": Sq, "Sk": Sk, "d": d, "dtype": "fp8",
+                  "num_splits": n, "kernel": ea.attn_kernel_name(B, H, Sq, d, 0, ea.ATTN_FP8_E4M3, n),
+                  "reps": reps, "splitkv": _stats(u1), "merge": _stats(u2),
+                  "total_us": round(t, 2), "alg_bytes": ab, "workspace_bytes_rw": 2 * wsb,
+                  "alg_gbs": round(ab / (t * 1e-6) / 1e9, 1),
+                  "with_ws_gbs": round((ab + 2 * wsb) / (t * 1e-6) / 1e9, 1),
+                  "pct_of_hbm": round(100.0 * ab / (t * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)})
+        return
+    raise ValueError(name)
+
+
+def summarize_sweep(path: str) -> str:
+    """Markdown table of the JSON lines written by --sweep."""
+    recs = [json.loads(l) for l in open(path) if l.strip().startswith("{")]
+    out = []
+    if recs and recs[0]["workload"] == "c5":
+        out += ["| n | kernel | splitkv median us | merge median us | total us | GB/s (alg.) | GB/s (with ws) | % of 8 TB/s |",
+                "|---|---|---|---|---|---|---|---|"]
+        for r in recs:
+            out.append(f"| {r['num_splits']} | {r['kernel']} | {r['splitkv']['median_us']} | "
+                       f"{r['merge']['median_us']} | {r['total_us']} | {r['alg_gbs']} | "
+                       f"{r['with_ws_gbs']} | {r['pct_of_hbm']} |")
+        return "\n".join(out)
+    out += ["| B | H | S | d | mask | kernel | median us | p10 / p90 us | TFLOP/s | FLOP/B | bound TFLOP/s | % of bound |",
+            "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in recs:
+        out.append(f"| {r['B']} | {r['H']} | {r['Sq']} | {r['d']} | {'causal' if r['causal'] else 'full'} | "
+                   f"{r['kernel']} | {r['median_us']} | {r['p10_us']} / {r['p90_us']} | "
+                   f"{r.get('tflops', '-')} | {r.get('flop_per_byte', '-')} | "
+                   f"{r.get('bound_tflops', '-')} ({r.get('bound', '-')}) | {r.get('pct_of_bound', '-')} |")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +328,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--sweep", choices=("c1", "c2", "c4", "c5"),
+                    help="per-case timing of a parity workload (JSON lines)")
+    ap.add_argument("--sweep-reps", type=int, default=30)
+    ap.add_argument("--summarize-sweep", metavar="JSONL")
     ap.add_argument("--summarize-stats", metavar="DIR",
                     help="print a table of a rocprofv3 --stats output directory and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -184,6 +339,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats))
+        return
+    if args.summarize_sweep:
+        print(summarize_sweep(args.summarize_sweep))
         return
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic, probe_mib=args.copy_probe_mib or 512,
@@ -193,6 +351,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep(args.sweep, args.sweep_reps, args.warmup)
+        return
 
     import torch
     import exact_attention_82_amd as ea
