@@ -122,6 +122,42 @@ def attn_merge(ws, num_splits, B, H, Sq, d, out=None, lse=None, stream=None):
     return out, lse
 
 
+def attn_bwd_workspace_bytes(B, H, Sq, d) -> int:
+    return int(_lib.load().attn_bwd_workspace_bytes(B, H, Sq, d))
+
+
+def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None,
+             ws=None, stream=None):
+    """Gradients (dQ, dK, dV), fp32, of O = attn_fwd(q, k, v) given O, lse and dO (fp32)."""
+    B, H, Sq, Sk, d, dt = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    for name, t, shape in (("o", o, (B, H, Sq, d)), ("dout", dout, (B, H, Sq, d)),
+                           ("lse", lse, (B, H, Sq))):
+        if tuple(t.shape) != shape or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 {list(shape)}")
+    dev = q.device
+    if dq is None:
+        dq = torch.empty((B, H, Sq, d), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((B, H, Sk, d), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty((B, H, Sk, d), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(attn_bwd_workspace_bytes(B, H, Sq, d), 16), dtype=torch.uint8,
+                         device=dev)
+    st = _lib.load().attn_bwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(o),
+                              ctypes_ptr(dout), ctypes_ptr(lse), ctypes_ptr(dq), ctypes_ptr(dk),
+                              ctypes_ptr(dv), ctypes_ptr(ws), ws.numel() * ws.element_size(),
+                              B, H, Sq, Sk, d, float(scale), int(causal), dt, _stream(stream))
+    _lib.check("attn_bwd", st)
+    return dq, dk, dv
+
+
+def attn_bwd_kernel_name(d, dtype, which):
+    return _lib.load().attn_bwd_kernel_name(d, dtype, which).decode()
+
+
 def workspace_views(ws, num_splits, B, H, Sq, d):
     """(m, l, u) views of a split-KV workspace, shaped [n,B,H,Sq], [n,B,H,Sq], [n,B,H,Sq,d]."""
     rows = B * H * Sq

@@ -155,6 +155,50 @@ attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o
   return launched(attn::launch_merge(a, stream));
 }
 
+size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int d) {
+  if (B < 1 || H < 1 || Sq < 1 || !supported_d(d)) return 0;
+  const int64_t rows = int64_t(B) * H * Sq;
+  if (rows * d >= kMaxIndex) return 0;
+  return attn::bwd_workspace_layout(rows, d).total;
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o,
+                     const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                     void* ws, size_t ws_bytes, int B, int H, int Sq, int Sk, int d,
+                     float scale, int causal, attn_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !ws) return ATTN_ERR_NULL;
+  attn_status st = check_shape(B, H, Sq, Sk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!attn::bwd_supported(dtype, d)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(ws))
+    return ATTN_ERR_ALIGN;
+  if ((causal != 0 && causal != 1) || !positive_finite(scale)) return ATTN_ERR_ARG;
+  const float sl2 = static_cast<float>(double(scale) * kLog2e);
+  if (!positive_finite(sl2)) return ATTN_ERR_ARG;
+  const int64_t rows = int64_t(B) * H * Sq;
+  const attn::BwdWorkspaceLayout w = attn::bwd_workspace_layout(rows, d);
+  if (ws_bytes < w.total) return ATTN_ERR_WORKSPACE;
+
+  char* base = static_cast<char*>(ws);
+  attn::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.do16 = reinterpret_cast<uint16_t*>(base + w.do_off);
+  a.dsum = reinterpret_cast<float*>(base + w.dsum_off);
+  a.lse2 = reinterpret_cast<float*>(base + w.lse2_off);
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = sl2;
+  return launched(attn::launch_bwd(a, stream));
+}
+
+const char* attn_bwd_kernel_name(int d, attn_dtype dtype, int which) {
+  if (!attn::bwd_supported(dtype, d) || which < 0 || which > 2) return "unsupported";
+  return attn::bwd_kernel_name(d, which);
+}
+
 int attn_block_m(int B, int H, int Sq, int d, int causal, attn_dtype dtype, int num_splits) {
   if (B < 1 || H < 1 || Sq < 1 || !supported_d(d) || !supported_dtype(dtype)) return 0;
   if (causal != 0 && causal != 1) return 0;

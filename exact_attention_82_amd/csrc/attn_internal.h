@@ -122,9 +122,49 @@ inline WorkspaceLayout workspace_layout(int64_t rows, int d, int n) {
   return w;
 }
 
+// Backward.  The caller's workspace holds dO rounded to bf16, the per-row term
+// D_i = sum_d dO_id O_id and lse in log2 units (+inf for rows with no visible key).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* o;
+  const float* dout;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  uint16_t* do16;  // workspace [B*H*Sq][d]
+  float* dsum;     // workspace [B*H*Sq]
+  float* lse2;     // workspace [B*H*Sq]
+  int B, H, Sq, Sk, d;
+  int causal;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+};
+
+struct BwdWorkspaceLayout {
+  size_t do_off, dsum_off, lse2_off, total;
+};
+
+inline BwdWorkspaceLayout bwd_workspace_layout(int64_t rows, int d) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  BwdWorkspaceLayout w;
+  w.do_off = 0;
+  w.dsum_off = up(size_t(rows) * size_t(d) * 2);
+  w.lse2_off = w.dsum_off + up(size_t(rows) * sizeof(float));
+  w.total = w.lse2_off + up(size_t(rows) * sizeof(float));
+  return w;
+}
+
+// The backward kernels exist for bf16 with d = 64 or 128.
+constexpr bool bwd_supported(int dtype, int d) { return dtype == 1 && (d == 64 || d == 128); }
+
 // Launchers (attn_kernels.hip).  Return a hipError_t value as int.
 int launch_fwd(const FwdArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
+int launch_bwd(const BwdArgs& a, void* stream);
+const char* bwd_kernel_name(int d, int which);  // which: 0 prologue, 1 dK/dV, 2 dQ
 // Compute units of the current device (cached per device), or 0 if unknown.
 int device_cu_count();
 const char* fwd_kernel_name(int dtype, int d, int split_mode, int sched);

@@ -1298,6 +1298,311 @@ hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+
+// ================================================================== backward
+// Gradients of exact attention with the probabilities recomputed from the forward's
+// lse, never stored: per (batch, head), with S = scale Q K^T masked as in the forward,
+//
+//   P = exp(S - lse),  dV = P^T dO,  dP = dO V^T,  dS = P (dP - D),  D_i = sum_d dO_id O_id,
+//   dQ = scale dS K,   dK = scale dS^T Q.
+//
+// dK and dV sum over queries and dQ over keys -- the "AI 大模型之 FlashAttention_02"
+// page, section "Training and deployment: backward consistency of split and reduction",
+// notes that the backward reduces across queries, the other direction from the forward.
+// Each sum stays inside one workgroup, so there are no atomics and the result does not
+// depend on timing:
+//
+//   attn_bwd_pre_kernel   per query row: D, dO rounded to bf16, lse in log2 units;
+//   attn_bwd_dkdv_kernel  one workgroup per 128 keys (four wavefronts of 32 keys, each
+//                         key in a lane position like a query row of the forward),
+//                         sweeping the query tiles of 32 rows that see those keys;
+//   attn_bwd_dq_kernel    one workgroup per 128 query rows, sweeping the visible key
+//                         tiles of 32, the forward's layout.
+//
+// Every product is a 32x32x16 bf16 MFMA with fp32 accumulation; P and dS are rounded
+// to bf16 as MFMA operands.  Tiles reach LDS by direct loads into two stages, each tile
+// once in the key-operand layout (rows read as the A operand) and, where its transpose
+// is needed, once more in the value-operand layout (read with ds_read_b64_tr_b16).
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void attn_bwd_pre_kernel(BwdArgs a) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  constexpr int TPR = D / 4;       // threads per row, four elements each
+  constexpr int RPB = 256 / TPR;   // rows per workgroup pass
+  const int64_t rows = int64_t(a.B) * a.H * a.Sq;
+  const int t = threadIdx.x % TPR;
+  // grid-stride over rows; the TPR threads of a row stay together
+  for (int64_t r = int64_t(blockIdx.x) * RPB + threadIdx.x / TPR; r < rows;
+       r += int64_t(gridDim.x) * RPB) {
+    const f32x4_t o4 = *reinterpret_cast<const f32x4_t*>(a.o + r * D + t * 4);
+    const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(a.dout + r * D + t * 4);
+    float dot = o4[0] * d4[0] + o4[1] * d4[1] + o4[2] * d4[2] + o4[3] * d4[3];
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, TPR);
+    *reinterpret_cast<bf16x4_t*>(a.do16 + r * D + t * 4) = __builtin_convertvector(d4, bf16x4_t);
+    if (t == 0) {
+      a.dsum[r] = dot;
+      const float l = a.lse[r];
+      a.lse2[r] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
+    }
+  }
+}
+
+// 64 consecutive floats from row i0 of a per-row buffer straight into LDS (lane L's at
+// dst[L]; rows past the buffer read as zeros).
+__device__ __forceinline__ void dma_floats(__amdgpu_buffer_rsrc_t rs, float* dst, int i0, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 4, (i0 + lane) * 4, 0, 0, 0);
+}
+
+// Four 16-byte chunks of the 32-float lse2 / D tile that lane (c, g) needs: the rows
+// 8*b + 4*g + 0..3 of its accumulator layout.
+__device__ __forceinline__ void load_row_terms(const float* t, int g, float (&x)[16]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(t + 8 * b + 4 * g);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[4 * b + r] = v[r];
+  }
+}
+
+__device__ __forceinline__ void pack_tile(const float (&x)[16], PTile<DT_BF16, 32>& pt) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f32x8_t v = {x[8 * h + 0], x[8 * h + 1], x[8 * h + 2], x[8 * h + 3],
+                 x[8 * h + 4], x[8 * h + 5], x[8 * h + 6], x[8 * h + 7]};
+    pt.pk[0][h] = __builtin_convertvector(v, bf16x8_t);
+  }
+}
+
+// Rows of a 32-row block of an output [S][D] from an accumulator X^T (d x rows) held in
+// the 32x32 layout: lane (c, g) writes row r0 + c, columns 32*db + 8*jj + 4*g + 0..3.
+template <int D>
+__device__ __forceinline__ void store_rows(float* out, int r0, int nrows, int c, int g,
+                                           const f32x16_t (&acc)[D / 32], float mul) {
+  if (r0 + c >= nrows) return;
+  float* dst = out + size_t(r0 + c) * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4_t v4 = {acc[db][4 * jj + 0], acc[db][4 * jj + 1], acc[db][4 * jj + 2],
+                          acc[db][4 * jj + 3]};
+      *reinterpret_cast<f32x4_t*>(dst + db * 32 + jj * 8 + g * 4) = v4 * mul;
+    }
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(D >= 128 ? 1 : 2, D >= 128 ? 1 : 2)))
+void attn_bwd_dkdv_kernel(BwdArgs a) {
+  using Op = Traits<DT_BF16>::Op;
+  using G = DmaGeo<DT_BF16, D, 32>;
+  constexpr int KSTEPS = D / 16;
+  constexpr int NDB = D / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31, g = lane >> 5;
+  const int nkt = ceil_div_i(a.Sk, kBlockM);
+  const int bh = blockIdx.x / nkt, kt = blockIdx.x % nkt;
+  const int key = kt * kBlockM + wave * 32 + c;  // this lane's key
+  const int off = a.Sk - a.Sq;
+  const float sl2 = a.scale_log2;
+
+  const size_t qo = size_t(bh) * a.Sq, ko = size_t(bh) * a.Sk;
+  const auto rq = make_rsrc(reinterpret_cast<const uint8_t*>(a.q) + qo * D * 2, uint32_t(a.Sq) * D * 2);
+  const auto rdo = make_rsrc(a.do16 + qo * D, uint32_t(a.Sq) * D * 2);
+  const auto rk = make_rsrc(reinterpret_cast<const uint8_t*>(a.k) + ko * D * 2, uint32_t(a.Sk) * D * 2);
+  const auto rv = make_rsrc(reinterpret_cast<const uint8_t*>(a.v) + ko * D * 2, uint32_t(a.Sk) * D * 2);
+  const auto rl = make_rsrc(a.lse2 + qo, uint32_t(a.Sq) * 4);
+  const auto rd = make_rsrc(a.dsum + qo, uint32_t(a.Sq) * 4);
+
+  // this wavefront's keys and values as B operands for the whole sweep (zeros past Sk)
+  Op kop[KSTEPS], vop[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const int boff = (key * D + ks * 16 + g * 8) * 2;
+    kop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b128(rk, boff, 0, 0));
+    vop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b128(rv, boff, 0, 0));
+  }
+  f32x16_t dkt[NDB], dvt[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    dkt[i] = f32x16_t{};
+    dvt[i] = f32x16_t{};
+  }
+  Pipe<DT_BF16, D, 32, kWaves> pipe(wave, lane);  // direct-to-LDS tile loads
+  const DmaLane<DT_BF16, D, 32>& ln = pipe.ln;
+
+  // two stages of {Q, dO} x {key layout, value layout} plus the lse2 and D rows
+  __shared__ __attribute__((aligned(1024))) uint8_t qk0[G::TILE], qv0[G::TILE], ok0[G::TILE], ov0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t qk1[G::TILE], qv1[G::TILE], ok1[G::TILE], ov1[G::TILE];
+  __shared__ __attribute__((aligned(256))) float ls0[64], ds0[64], ls1[64], ds1[64];
+
+  // query rows that see a key of this workgroup: i >= first key - off (causal)
+  const int ibeg = a.causal ? (max(0, kt * kBlockM - off) / 32) * 32 : 0;
+  const int ntiles = ibeg < a.Sq ? ceil_div_i(a.Sq - ibeg, 32) : 0;
+
+  auto issue = [&](int i0, uint8_t* qk, uint8_t* qv, uint8_t* okk, uint8_t* ovv, float* ls, float* ds)
+      __attribute__((always_inline)) {
+    pipe.issue_k(rq, i0, qk);
+    pipe.issue_v(rq, i0, qv);
+    pipe.issue_k(rdo, i0, okk);
+    pipe.issue_v(rdo, i0, ovv);
+    if (wave == 0) dma_floats(rl, ls, i0, lane);
+    if (wave == 1) dma_floats(rd, ds, i0, lane);
+  };
+  auto compute = [&](int i0, const uint8_t* qk, const uint8_t* qv, const uint8_t* okk,
+                     const uint8_t* ovv, const float* ls, const float* ds) __attribute__((always_inline)) {
+    f32x16_t st[1], dp[1];
+    qk_dma<DT_BF16, D, 32>(st, qk, kop, ln);   // S  [query][key]
+    qk_dma<DT_BF16, D, 32>(dp, okk, vop, ln);  // dP [query][key]
+    float l2[16], dd[16], pv[16], sv[16];
+    load_row_terms(ls, g, l2);
+    load_row_terms(ds, g, dd);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int i = i0 + 8 * (e >> 2) + 4 * g + (e & 3);
+      const bool vis = i < a.Sq && key < a.Sk && (!a.causal || key <= i + off);
+      const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[0][e], sl2, -l2[e])) : 0.0f;
+      pv[e] = p;
+      sv[e] = p * (dp[0][e] - dd[e]);
+    }
+    PTile<DT_BF16, 32> pp, ps;
+    pack_tile(pv, pp);
+    pack_tile(sv, ps);
+    pv_dma<DT_BF16, D, 32>(dvt, pp, ovv, ln);  // dV^T += dO^T P
+    pv_dma<DT_BF16, D, 32>(dkt, ps, qv, ln);   // dK^T += Q^T dS
+  };
+
+  if (ntiles > 0) issue(ibeg, qk0, qv0, ok0, ov0, ls0, ds0);
+  wait_vmem();
+  block_sync();
+  for (int t = 0; t < ntiles; t += 2) {
+    const int i0 = ibeg + t * 32;
+    if (t + 1 < ntiles) issue(i0 + 32, qk1, qv1, ok1, ov1, ls1, ds1);
+    compute(i0, qk0, qv0, ok0, ov0, ls0, ds0);
+    wait_vmem();
+    block_sync();
+    if (t + 1 < ntiles) {
+      if (t + 2 < ntiles) issue(i0 + 64, qk0, qv0, ok0, ov0, ls0, ds0);
+      compute(i0 + 32, qk1, qv1, ok1, ov1, ls1, ds1);
+      wait_vmem();
+      block_sync();
+    }
+  }
+  const int kw0 = kt * kBlockM + wave * 32;
+  store_rows<D>(a.dk + ko * D, kw0, a.Sk, c, g, dkt, a.scale);
+  store_rows<D>(a.dv + ko * D, kw0, a.Sk, c, g, dvt, 1.0f);
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(BwdArgs a) {
+  using Op = Traits<DT_BF16>::Op;
+  using G = DmaGeo<DT_BF16, D, 32>;
+  constexpr int KSTEPS = D / 16;
+  constexpr int NDB = D / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31, g = lane >> 5;
+  const int nqt = ceil_div_i(a.Sq, kBlockM);
+  const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
+  const int r0 = qt * kBlockM + wave * 32;
+  const int row = r0 + c;  // this lane's query row
+  const int off = a.Sk - a.Sq;
+  const float sl2 = a.scale_log2;
+
+  const size_t qo = size_t(bh) * a.Sq, ko = size_t(bh) * a.Sk;
+  const auto rq = make_rsrc(reinterpret_cast<const uint8_t*>(a.q) + qo * D * 2, uint32_t(a.Sq) * D * 2);
+  const auto rdo = make_rsrc(a.do16 + qo * D, uint32_t(a.Sq) * D * 2);
+  const auto rk = make_rsrc(reinterpret_cast<const uint8_t*>(a.k) + ko * D * 2, uint32_t(a.Sk) * D * 2);
+  const auto rv = make_rsrc(reinterpret_cast<const uint8_t*>(a.v) + ko * D * 2, uint32_t(a.Sk) * D * 2);
+
+  Op qop[KSTEPS], dop[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const int boff = (row * D + ks * 16 + g * 8) * 2;
+    qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b128(rq, boff, 0, 0));
+    dop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b128(rdo, boff, 0, 0));
+  }
+  const float l2 = row < a.Sq ? a.lse2[qo + row] : __builtin_inff();
+  const float dd = row < a.Sq ? a.dsum[qo + row] : 0.0f;
+  f32x16_t dqt[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dqt[i] = f32x16_t{};
+  Pipe<DT_BF16, D, 32, kWaves> pipe(wave, lane);  // direct-to-LDS tile loads
+  const DmaLane<DT_BF16, D, 32>& ln = pipe.ln;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t kk0[G::TILE], kv0[G::TILE], vk0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kk1[G::TILE], kv1[G::TILE], vk1[G::TILE];
+
+  int kend = a.Sk;
+  if (a.causal) {
+    const int last_row = min((qt + 1) * kBlockM, a.Sq) - 1;
+    kend = max(0, min(a.Sk, last_row + off + 1));
+  }
+  const int ntiles = ceil_div_i(kend, 32);
+
+  auto issue = [&](int k0, uint8_t* kk, uint8_t* kv, uint8_t* vk) __attribute__((always_inline)) {
+    pipe.issue_k(rk, k0, kk);
+    pipe.issue_v(rk, k0, kv);
+    pipe.issue_k(rv, k0, vk);
+  };
+  auto compute = [&](int k0, const uint8_t* kk, const uint8_t* kv, const uint8_t* vk)
+      __attribute__((always_inline)) {
+    f32x16_t st[1], dpt[1];
+    qk_dma<DT_BF16, D, 32>(st, kk, qop, ln);   // S^T  [key][query]
+    qk_dma<DT_BF16, D, 32>(dpt, vk, dop, ln);  // dP^T [key][query]
+    float sv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int kj = k0 + 8 * (e >> 2) + 4 * g + (e & 3);
+      const bool vis = kj < kend && row < a.Sq && (!a.causal || kj <= row + off);
+      const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[0][e], sl2, -l2)) : 0.0f;
+      sv[e] = p * (dpt[0][e] - dd);
+    }
+    PTile<DT_BF16, 32> ps;
+    pack_tile(sv, ps);
+    pv_dma<DT_BF16, D, 32>(dqt, ps, kv, ln);  // dQ^T += K^T dS^T
+  };
+
+  if (ntiles > 0) issue(0, kk0, kv0, vk0);
+  wait_vmem();
+  block_sync();
+  for (int t = 0; t < ntiles; t += 2) {
+    const int k0 = t * 32;
+    if (t + 1 < ntiles) issue(k0 + 32, kk1, kv1, vk1);
+    compute(k0, kk0, kv0, vk0);
+    wait_vmem();
+    block_sync();
+    if (t + 1 < ntiles) {
+      if (t + 2 < ntiles) issue(k0 + 64, kk0, kv0, vk0);
+      compute(k0 + 32, kk1, kv1, vk1);
+      wait_vmem();
+      block_sync();
+    }
+  }
+  store_rows<D>(a.dq + qo * D, r0, a.Sq, c, g, dqt, a.scale);
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
+  const int64_t rows = int64_t(a.B) * a.H * a.Sq;
+  constexpr int RPB = 256 / (D / 4);
+  const int64_t pre = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL(attn_bwd_pre_kernel<D>, dim3(unsigned(pre < 65536 ? pre : 65536)), dim3(256), 0, s, a);
+  const int64_t nkv = int64_t(a.B) * a.H * ((a.Sk + kBlockM - 1) / kBlockM);
+  if (nkv > 0) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(unsigned(nkv)), dim3(kThreads), 0, s, a);
+  const int64_t nq = int64_t(a.B) * a.H * ((a.Sq + kBlockM - 1) / kBlockM);
+  if (nq > 0) hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(unsigned(nq)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 }  // namespace
 
 int launch_fwd(const FwdArgs& a, void* stream) {
@@ -1320,6 +1625,23 @@ int launch_merge(const MergeArgs& a, void* stream) {
     default: return int(hipErrorInvalidValue);
   }
   return int(hipGetLastError());
+}
+
+int launch_bwd(const BwdArgs& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (a.d) {
+    case 64: return int(launch_bwd_d<64>(a, s));
+    case 128: return int(launch_bwd_d<128>(a, s));
+  }
+  return int(hipErrorInvalidValue);
+}
+
+const char* bwd_kernel_name(int d, int which) {
+  static const char* names[2][3] = {
+      {"attn_bwd_pre_d64", "attn_bwd_dkdv_bf16_d64_bn128_bm32", "attn_bwd_dq_bf16_d64_bm128_bn32"},
+      {"attn_bwd_pre_d128", "attn_bwd_dkdv_bf16_d128_bn128_bm32", "attn_bwd_dq_bf16_d128_bm128_bn32"}};
+  if ((d != 64 && d != 128) || which < 0 || which > 2) return "";
+  return names[d == 64 ? 0 : 1][which];
 }
 
 int device_cu_count() {

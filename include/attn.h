@@ -133,6 +133,49 @@ attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o
                        int B, int H, int Sq, int d, void* stream);
 
 /*
+ * attn_bwd_workspace_bytes -- bytes of the workspace attn_bwd needs for this shape, or 0
+ * if an argument is out of range.  Layout (each section at a multiple of 256 bytes from
+ * the base), R = B*H*Sq rows: dO rounded to bf16 [R][d], D = sum_d dO*O [R] (fp32), lse
+ * in log2 units [R] (fp32).  Contents are scratch between calls.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int d);
+
+/*
+ * attn_bwd -- gradients of the forward above with respect to Q, K and V.
+ *
+ * Given the forward's inputs, its outputs O and lse (from attn_fwd with the same
+ * arguments) and dO = dL/dO, writes dQ, dK, dV for O = softmax(scale * Q K^T + mask) V:
+ *     P = exp(scale * Q K^T - lse) (0 where masked),  dV = P^T dO,  dP = dO V^T,
+ *     dS = P * (dP - D) with D_i = sum_d dO_id O_id,  dQ = scale * dS K,  dK = scale * dS^T Q.
+ * The probabilities are recomputed from lse, never stored.  dK and dV sum over the
+ * queries and dQ over the keys, each inside one workgroup: no atomics, and the result
+ * does not depend on timing ("AI 大模型之 FlashAttention_02", section "Training and
+ * deployment: backward consistency of split and reduction": the backward reduces across
+ * queries, the other direction from the forward's split).  Rows with no visible key
+ * (lse = -inf) get dQ = 0 and contribute nothing.
+ *
+ *   q, k, v      device pointers, [B,H,Sq,d], [B,H,Sk,d], [B,H,Sk,d], bf16 (dtype ATTN_BF16)
+ *   o, dout      device pointers, fp32 [B,H,Sq,d]: forward output and upstream gradient
+ *   lse          device pointer, fp32 [B,H,Sq]: forward log-sum-exp (natural log)
+ *   dq, dk, dv   device pointers, fp32 outputs [B,H,Sq,d], [B,H,Sk,d], [B,H,Sk,d]
+ *   ws, ws_bytes device workspace of at least attn_bwd_workspace_bytes(B, H, Sq, d)
+ *   scale, causal as for attn_fwd
+ * Supported: dtype ATTN_BF16 with d = 64 or 128 (else ATTN_ERR_UNSUPPORTED).  All
+ * pointers 16-byte aligned, buffers contiguous and not overlapping.  dO is used rounded
+ * to bf16, and P and dS are rounded to bf16 as operands of the products (fp32
+ * accumulation).  Asynchronous on `stream` (three launches); the library allocates
+ * nothing.  Errors are returned before any launch.
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o,
+                     const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                     void* ws, size_t ws_bytes, int B, int H, int Sq, int Sk, int d,
+                     float scale, int causal, attn_dtype dtype, void* stream);
+
+/* Name of a kernel attn_bwd launches: which = 0 prologue, 1 dK/dV, 2 dQ ("unsupported"
+ * if none). */
+const char* attn_bwd_kernel_name(int d, attn_dtype dtype, int which);
+
+/*
  * Launch plan queries.  num_splits = 0 describes attn_fwd; num_splits >= 1 describes
  * attn_fwd_splitkv with that many chunks.  A call launches one four-wavefront workgroup
  * per 128 query rows (times num_splits), except causal bf16 calls with d <= 128 whose
