@@ -1,7 +1,7 @@
 """Benchmark of the exact attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
-    python bench.py --sweep {c1,c2,c4,c5} > sweep.jsonl     (per-case timing, see below)
+    python bench.py --sweep {c1,c2,c4,c5,bwd} > sweep.jsonl (per-case timing, see below)
     python bench.py --summarize-sweep sweep.jsonl           (markdown table of those lines)
 
 Workload (default): B=1, H=8, Sq=Sk=8192, d=128, Q/K/V i.i.d. N(0,1) rounded to bf16,
@@ -27,7 +27,11 @@ B=1,H=2,S=128,d=64) reports microseconds; c2 and the 36 c4 cases (d in 64/128/25
 512/1000/2048, B in 1/8, H=16, bf16 with 1 % of query rows scaled by 30) report TFLOP/s
 against min(bf16 MFMA peak, intensity x 8 TB/s); c5 (fp8 B=1,H=8,Sq=128,Sk=32768,d=128)
 times attn_fwd_splitkv and attn_merge apart for n = 1, 4, 16 and reports the algorithmic
-bytes (Q, K, V read once, O and lse written once) per second against 8 TB/s.
+bytes (Q, K, V read once, O and lse written once) per second against 8 TB/s.  bwd times
+attn_bwd (three launches: prologue, dK/dV, dQ) at the c3 and c2 shapes with inputs
+resident (repeated calls), counting 10*B*H*Sq*Sk*d FLOPs (2.5x the forward's: the five
+products S, dP, dV, dK, dQ; half causal) against the bf16 MFMA peak, and times the fp64
+oracle's backward on one head beside it.
 """
 from __future__ import annotations
 
@@ -265,6 +269,55 @@ def sweep(name: str, reps: int, warmup: int):
             del q, k, v, o, lse
             torch.cuda.empty_cache()
         return
+    if name == "bwd":
+        import oracle
+        for (B, H, S, d, seed) in ((1, 8, 8192, 128, 3), (8, 32, 2048, 64, 2)):
+            inp = si.make_attention_inputs(B, H, S, S, d, seed=seed, dtype="bf16")
+            q, k, v = to_dev(inp)
+            rng = np.random.default_rng(seed + 1000)
+            do = torch.from_numpy(rng.standard_normal((B, H, S, d), dtype=np.float32)).to(dev)
+            scale = float(np.float32(1.0 / np.sqrt(d)))
+            ws = torch.empty(ea.attn_bwd_workspace_bytes(B, H, S, d), dtype=torch.uint8, device=dev)
+            dq = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
+            dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+            for causal in (False, True):
+                o, lse = ea.attn_fwd(q, k, v, scale=scale, causal=causal)
+                fn = lambda: ea.attn_bwd(q, k, v, o, lse, do, scale=scale, causal=causal,
+                                         dq=dq, dk=dk, dv=dv, ws=ws)
+                for _ in range(warmup):
+                    fn()
+                torch.cuda.synchronize()
+                us = []
+                for _ in range(reps):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    us.append(e0.elapsed_time(e1) * 1e3)
+                us = np.array(us)
+                fl = 10.0 * B * H * S * S * d / (2.0 if causal else 1.0)
+                tf = fl / (float(np.median(us)) * 1e-6) / 1e12
+                rec = {"workload": "bwd", "B": B, "H": H, "Sq": S, "Sk": S, "d": d, "dtype": "bf16",
+                       "causal": causal, "kernel": " + ".join(ea.attn_bwd_kernel_name(d, ea.ATTN_BF16, w)
+                                                             for w in range(3)),
+                       "reps": reps, **_stats(us), "tflops": round(tf, 2),
+                       "flop_per_byte": None, "bound_tflops": PEAK_BF16_TFLOPS, "bound": "mfma",
+                       "pct_of_bound": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
+                if B == 1:
+                    # the oracle's backward on one head of the same inputs, timed on the host
+                    h0 = time.perf_counter()
+                    oracle.attention_bwd(inp.q64[0, 0], inp.k64[0, 0], inp.v64[0, 0],
+                                         do[0, 0].cpu().numpy(), scale, causal)
+                    dt = time.perf_counter() - h0
+                    rec["cpu_baseline"] = {"value": round(10.0 * S * S * d / (2.0 if causal else 1.0) / dt / 1e12, 4),
+                                           "unit": "TFLOPS", "kind": "oracle",
+                                           "sample": f"one head (S={S}, d={d}), fp64 NumPy, {dt:.2f} s"}
+                emit(rec)
+            del q, k, v, do, ws, dq, dk, dv
+            torch.cuda.empty_cache()
+        return
     if name == "c5":
         B, H, Sq, Sk, d = 1, 8, 128, 32768, 128
         inp = si.make_attention_inputs(B, H, Sq, Sk, d, seed=5, dtype="fp8")
@@ -315,6 +368,11 @@ def summarize_sweep(path: str) -> str:
                    f"{r['kernel']} | {r['median_us']} | {r['p10_us']} / {r['p90_us']} | "
                    f"{r.get('tflops', '-')} | {r.get('flop_per_byte', '-')} | "
                    f"{r.get('bound_tflops', '-')} ({r.get('bound', '-')}) | {r.get('pct_of_bound', '-')} |")
+    for r in recs:
+        if "cpu_baseline" in r:
+            cb = r["cpu_baseline"]
+            out.append(f"\ncpu_baseline ({'causal' if r['causal'] else 'full'}): {cb['value']} "
+                       f"{cb['unit']}, {cb['kind']}, {cb['sample']}")
     return "\n".join(out)
 
 
@@ -328,7 +386,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
-    ap.add_argument("--sweep", choices=("c1", "c2", "c4", "c5"),
+    ap.add_argument("--sweep", choices=("c1", "c2", "c4", "c5", "bwd"),
                     help="per-case timing of a parity workload (JSON lines)")
     ap.add_argument("--sweep-reps", type=int, default=30)
     ap.add_argument("--summarize-sweep", metavar="JSONL")

@@ -1394,9 +1394,56 @@ __device__ __forceinline__ void store_rows(float* out, int r0, int nrows, int c,
     }
 }
 
+// Row-operand offset into a tile stored in the value layout: lane (c, g) reads 16-byte
+// chunk 2*ks + g of row c as `tile + (x ^ (ks << 5))`, the same access the key layout
+// gives with DmaLane::kx, so one copy of a tile serves both its row reads and its
+// transposed reads.
+template <int D>
+__device__ __forceinline__ int row_lane_offset_vlayout(int lane) {
+  constexpr int ROWB = D * 2;
+  const int c = lane & 31, g = lane >> 5;
+  return c * ROWB + ((g ^ swz_v<DT_BF16, ROWB>(c)) << 4);
+}
+
+// One 32x32 block of X Y^T from two LDS tiles read as rows: X rows from `xt` (value
+// layout, lane offset xv) as the A operand, Y rows from `yt` (key layout, lane offset ky)
+// as the B operand.
+template <int D>
+__device__ __forceinline__ f32x16_t rows_product_lds(const uint8_t* xt, int xv, const uint8_t* yt, int ky) {
+  using Op = Traits<DT_BF16>::Op;
+  f32x16_t acc = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const Op a = *reinterpret_cast<const Op*>(xt + (xv ^ (ks << 5)));
+    const Op b = *reinterpret_cast<const Op*>(yt + (ky ^ (ks << 5)));
+    acc = Traits<DT_BF16>::mfma(a, b, acc);
+  }
+  return acc;
+}
+
+// Same with the B operand already in registers.
+template <int D>
+__device__ __forceinline__ f32x16_t rows_product_reg(const uint8_t* xt, int xv,
+                                                     const Traits<DT_BF16>::Op (&b)[D / 16]) {
+  using Op = Traits<DT_BF16>::Op;
+  f32x16_t acc = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    acc = Traits<DT_BF16>::mfma(*reinterpret_cast<const Op*>(xt + (xv ^ (ks << 5))), b[ks], acc);
+  return acc;
+}
+
+// dK and dV of 128 keys per workgroup.  Each wavefront's 32 keys sit in lane position;
+// their K rows stay in registers (B operand of S = Q K^T) and their V rows in an LDS
+// block loaded once (B operand of dP = dO V^T).  Query tiles of 32 rows stream through
+// two LDS stages, Q and dO each stored once in the value layout: read as rows for S and
+// dP, transposed for dK^T += Q^T dS and dV^T += dO^T P.  Two workgroups fit a CU (LDS
+// and 256 registers per wavefront).  Causal: key tile kt sees the queries from
+// kt*128 - (Sk - Sq) on, so workgroups i and i + grid/2, which share a CU, take
+// complementary key tiles.
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(D >= 128 ? 1 : 2, D >= 128 ? 1 : 2)))
+                          amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(BwdArgs a) {
   using Op = Traits<DT_BF16>::Op;
   using G = DmaGeo<DT_BF16, D, 32>;
@@ -1406,9 +1453,16 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, g = lane >> 5;
+  const int BH = a.B * a.H;
   const int nkt = ceil_div_i(a.Sk, kBlockM);
-  const int bh = blockIdx.x / nkt, kt = blockIdx.x % nkt;
-  const int key = kt * kBlockM + wave * 32 + c;  // this lane's key
+  const int bh = blockIdx.x % BH;
+  int kt = blockIdx.x / BH;
+  if (a.causal) {
+    const int half = (nkt + 1) / 2;
+    kt = kt < half ? kt : nkt - 1 - (kt - half);
+  }
+  const int kw0 = kt * kBlockM + wave * 32;  // first key of this wavefront
+  const int key = kw0 + c;                   // this lane's key
   const int off = a.Sk - a.Sq;
   const float sl2 = a.scale_log2;
 
@@ -1420,14 +1474,10 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const auto rl = make_rsrc(a.lse2 + qo, uint32_t(a.Sq) * 4);
   const auto rd = make_rsrc(a.dsum + qo, uint32_t(a.Sq) * 4);
 
-  // this wavefront's keys and values as B operands for the whole sweep (zeros past Sk)
-  Op kop[KSTEPS], vop[KSTEPS];
+  Op kop[KSTEPS];  // this wavefront's keys, B operand of S (zeros past Sk)
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    const int boff = (key * D + ks * 16 + g * 8) * 2;
-    kop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b128(rk, boff, 0, 0));
-    vop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b128(rv, boff, 0, 0));
-  }
+  for (int ks = 0; ks < KSTEPS; ++ks)
+    kop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b128(rk, (key * D + ks * 16 + g * 8) * 2, 0, 0));
   f32x16_t dkt[NDB], dvt[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) {
@@ -1436,65 +1486,68 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   }
   Pipe<DT_BF16, D, 32, kWaves> pipe(wave, lane);  // direct-to-LDS tile loads
   const DmaLane<DT_BF16, D, 32>& ln = pipe.ln;
+  const int xv = row_lane_offset_vlayout<D>(lane);
 
-  // two stages of {Q, dO} x {key layout, value layout} plus the lse2 and D rows
-  __shared__ __attribute__((aligned(1024))) uint8_t qk0[G::TILE], qv0[G::TILE], ok0[G::TILE], ov0[G::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t qk1[G::TILE], qv1[G::TILE], ok1[G::TILE], ov1[G::TILE];
+  // the workgroup's V rows (key layout), then two stages of {Q, dO} (value layout)
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0[G::TILE], vb1[G::TILE], vb2[G::TILE], vb3[G::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t q0s[G::TILE], o0s[G::TILE], q1s[G::TILE], o1s[G::TILE];
   __shared__ __attribute__((aligned(256))) float ls0[64], ds0[64], ls1[64], ds1[64];
+  const uint8_t* vmine = wave == 0 ? vb0 : wave == 1 ? vb1 : wave == 2 ? vb2 : vb3;
 
-  // query rows that see a key of this workgroup: i >= first key - off (causal)
   const int ibeg = a.causal ? (max(0, kt * kBlockM - off) / 32) * 32 : 0;
   const int ntiles = ibeg < a.Sq ? ceil_div_i(a.Sq - ibeg, 32) : 0;
 
-  auto issue = [&](int i0, uint8_t* qk, uint8_t* qv, uint8_t* okk, uint8_t* ovv, float* ls, float* ds)
-      __attribute__((always_inline)) {
-    pipe.issue_k(rq, i0, qk);
-    pipe.issue_v(rq, i0, qv);
-    pipe.issue_k(rdo, i0, okk);
-    pipe.issue_v(rdo, i0, ovv);
+  auto issue = [&](int i0, uint8_t* qs, uint8_t* os, float* ls, float* ds) __attribute__((always_inline)) {
+    pipe.issue_v(rq, i0, qs);
+    pipe.issue_v(rdo, i0, os);
     if (wave == 0) dma_floats(rl, ls, i0, lane);
     if (wave == 1) dma_floats(rd, ds, i0, lane);
   };
-  auto compute = [&](int i0, const uint8_t* qk, const uint8_t* qv, const uint8_t* okk,
-                     const uint8_t* ovv, const float* ls, const float* ds) __attribute__((always_inline)) {
-    f32x16_t st[1], dp[1];
-    qk_dma<DT_BF16, D, 32>(st, qk, kop, ln);   // S  [query][key]
-    qk_dma<DT_BF16, D, 32>(dp, okk, vop, ln);  // dP [query][key]
-    float l2[16], dd[16], pv[16], sv[16];
-    load_row_terms(ls, g, l2);
-    load_row_terms(ds, g, dd);
+  auto compute = [&](int i0, const uint8_t* qs, const uint8_t* os, const float* ls, const float* ds)
+      __attribute__((always_inline)) {
+    const f32x16_t st = rows_product_reg<D>(qs, xv, kop);              // S  [query][key]
+    const f32x16_t dp = rows_product_lds<D>(os, xv, vmine, ln.kx);     // dP [query][key]
+    float pv[16], sv[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int i = i0 + 8 * (e >> 2) + 4 * g + (e & 3);
-      const bool vis = i < a.Sq && key < a.Sk && (!a.causal || key <= i + off);
-      const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[0][e], sl2, -l2[e])) : 0.0f;
-      pv[e] = p;
-      sv[e] = p * (dp[0][e] - dd[e]);
+    for (int b = 0; b < 4; ++b) {
+      const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(ls + 8 * b + 4 * g);
+      const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(ds + 8 * b + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = 4 * b + r;
+        const int i = i0 + 8 * b + 4 * g + r;
+        const bool vis = i < a.Sq && key < a.Sk && (!a.causal || key <= i + off);
+        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[e], sl2, -l4[r])) : 0.0f;
+        pv[e] = p;
+        sv[e] = p * (dp[e] - d4[r]);
+      }
     }
     PTile<DT_BF16, 32> pp, ps;
     pack_tile(pv, pp);
     pack_tile(sv, ps);
-    pv_dma<DT_BF16, D, 32>(dvt, pp, ovv, ln);  // dV^T += dO^T P
-    pv_dma<DT_BF16, D, 32>(dkt, ps, qv, ln);   // dK^T += Q^T dS
+    pv_dma<DT_BF16, D, 32>(dvt, pp, os, ln);  // dV^T += dO^T P
+    pv_dma<DT_BF16, D, 32>(dkt, ps, qs, ln);  // dK^T += Q^T dS
   };
 
-  if (ntiles > 0) issue(ibeg, qk0, qv0, ok0, ov0, ls0, ds0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    pipe.issue_k(rv, kt * kBlockM + 32 * i, i == 0 ? vb0 : i == 1 ? vb1 : i == 2 ? vb2 : vb3);
+  if (ntiles > 0) issue(ibeg, q0s, o0s, ls0, ds0);
   wait_vmem();
   block_sync();
   for (int t = 0; t < ntiles; t += 2) {
     const int i0 = ibeg + t * 32;
-    if (t + 1 < ntiles) issue(i0 + 32, qk1, qv1, ok1, ov1, ls1, ds1);
-    compute(i0, qk0, qv0, ok0, ov0, ls0, ds0);
+    if (t + 1 < ntiles) issue(i0 + 32, q1s, o1s, ls1, ds1);
+    compute(i0, q0s, o0s, ls0, ds0);
     wait_vmem();
     block_sync();
     if (t + 1 < ntiles) {
-      if (t + 2 < ntiles) issue(i0 + 64, qk0, qv0, ok0, ov0, ls0, ds0);
-      compute(i0 + 32, qk1, qv1, ok1, ov1, ls1, ds1);
+      if (t + 2 < ntiles) issue(i0 + 64, q0s, o0s, ls0, ds0);
+      compute(i0 + 32, q1s, o1s, ls1, ds1);
       wait_vmem();
       block_sync();
     }
   }
-  const int kw0 = kt * kBlockM + wave * 32;
   store_rows<D>(a.dk + ko * D, kw0, a.Sk, c, g, dkt, a.scale);
   store_rows<D>(a.dv + ko * D, kw0, a.Sk, c, g, dvt, 1.0f);
 }
@@ -1511,8 +1564,14 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, g = lane >> 5;
+  const int BH = a.B * a.H;
   const int nqt = ceil_div_i(a.Sq, kBlockM);
-  const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
+  const int bh = blockIdx.x % BH;
+  int qt = blockIdx.x / BH;
+  if (a.causal) {  // longest (last) query tiles first, paired with short ones per CU
+    const int half = (nqt + 1) / 2;
+    qt = qt < half ? nqt - 1 - qt : qt - half;
+  }
   const int r0 = qt * kBlockM + wave * 32;
   const int row = r0 + c;  // this lane's query row
   const int off = a.Sk - a.Sq;

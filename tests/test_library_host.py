@@ -131,3 +131,26 @@ def test_per_head_slices_must_fit_32bit_offsets(lib):
     # 2^24 keys x 128 x bf16 = 4 GiB per head: refused before any launch
     assert fwd(lib, Sq=8, Sk=1 << 24, d=128) == 2
     assert fwd(lib, Sq=1 << 23, Sk=8, d=256, dtype=0) == 2
+
+
+def test_backward_refuses_bad_arguments_and_lays_out_its_workspace(lib):
+    B, H, Sq, Sk, d = 1, 2, 16, 24, 128
+    rows = B * H * Sq
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    need = lib.attn_bwd_workspace_bytes(B, H, Sq, d)
+    assert need == up(rows * d * 2) + up(rows * 4) + up(rows * 4)
+    assert lib.attn_bwd_workspace_bytes(B, H, Sq, 100) == 0
+    DO, DQ, DK, DV, W = 0x60000, 0x70000, 0x80000, 0x90000, 0xA0000
+
+    def bwd(q=Q, dout=DO, dq=DQ, ws=W, nb=need, d=d, dtype=1, causal=0, scale=0.125):
+        return lib.attn_bwd(q, K, V, O, dout, L, dq, DK, DV, ws, nb, B, H, Sq, Sk, d, scale,
+                            causal, dtype, None)
+    assert bwd(q=None) == 1 and bwd(dout=None) == 1 and bwd(dq=None) == 1 and bwd(ws=None) == 1
+    assert bwd(nb=need - 1) == 5
+    assert bwd(d=256) == 4          # the backward covers d = 64 and 128
+    assert bwd(dtype=0) == 4 and bwd(dtype=2) == 4   # bf16 only
+    assert bwd(dq=DQ + 4) == 3 and bwd(ws=W + 8) == 3
+    assert bwd(causal=3) == 7 and bwd(scale=-1.0) == 7
+    names = {lib.attn_bwd_kernel_name(d, 1, w).decode() for w in range(3)}
+    assert all(n.startswith("attn_bwd_") for n in names) and len(names) == 3
+    assert lib.attn_bwd_kernel_name(d, 0, 1).decode() == "unsupported"
