@@ -117,6 +117,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// Wait until at most N vector memory operations of this wavefront are in flight.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Workgroup barrier without the release fence of __syncthreads(): the fence would make
 // the compiler wait for every direct-to-LDS load still in flight (vmcnt(0)), including
@@ -1598,8 +1603,13 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   Pipe<DT_BF16, D, 32, kWaves> pipe(wave, lane);  // direct-to-LDS tile loads
   const DmaLane<DT_BF16, D, 32>& ln = pipe.ln;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t kk0[G::TILE], kv0[G::TILE], vk0[G::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kk1[G::TILE], kv1[G::TILE], vk1[G::TILE];
+  // three stages of {K (value layout), V (key layout)}: tile t+2 is requested while tile t
+  // is computed, so a tile's loads have two iterations to land
+  __shared__ __attribute__((aligned(1024))) uint8_t kv0[G::TILE], vk0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kv1[G::TILE], vk1[G::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kv2[G::TILE], vk2[G::TILE];
+  const int xv = row_lane_offset_vlayout<D>(lane);
+  constexpr int LPT = 2 * (G::TILE / 1024 / kWaves);  // loads per wavefront per tile
 
   int kend = a.Sk;
   if (a.causal) {
@@ -1608,22 +1618,26 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   }
   const int ntiles = ceil_div_i(kend, 32);
 
-  auto issue = [&](int k0, uint8_t* kk, uint8_t* kv, uint8_t* vk) __attribute__((always_inline)) {
-    pipe.issue_k(rk, k0, kk);
+  auto kvst = [&](int j) __attribute__((always_inline)) -> uint8_t* {
+    return j % 3 == 0 ? kv0 : j % 3 == 1 ? kv1 : kv2;
+  };
+  auto vkst = [&](int j) __attribute__((always_inline)) -> uint8_t* {
+    return j % 3 == 0 ? vk0 : j % 3 == 1 ? vk1 : vk2;
+  };
+  auto issue = [&](int k0, uint8_t* kv, uint8_t* vk) __attribute__((always_inline)) {
     pipe.issue_v(rk, k0, kv);
     pipe.issue_k(rv, k0, vk);
   };
-  auto compute = [&](int k0, const uint8_t* kk, const uint8_t* kv, const uint8_t* vk)
-      __attribute__((always_inline)) {
-    f32x16_t st[1], dpt[1];
-    qk_dma<DT_BF16, D, 32>(st, kk, qop, ln);   // S^T  [key][query]
-    qk_dma<DT_BF16, D, 32>(dpt, vk, dop, ln);  // dP^T [key][query]
+  auto compute = [&](int k0, const uint8_t* kv, const uint8_t* vk) __attribute__((always_inline)) {
+    const f32x16_t st = rows_product_reg<D>(kv, xv, qop);  // S^T  [key][query]
+    f32x16_t dpt[1];
+    qk_dma<DT_BF16, D, 32>(dpt, vk, dop, ln);              // dP^T [key][query]
     float sv[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int kj = k0 + 8 * (e >> 2) + 4 * g + (e & 3);
       const bool vis = kj < kend && row < a.Sq && (!a.causal || kj <= row + off);
-      const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[0][e], sl2, -l2)) : 0.0f;
+      const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[e], sl2, -l2)) : 0.0f;
       sv[e] = p * (dpt[0][e] - dd);
     }
     PTile<DT_BF16, 32> ps;
@@ -1631,20 +1645,22 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     pv_dma<DT_BF16, D, 32>(dqt, ps, kv, ln);  // dQ^T += K^T dS^T
   };
 
-  if (ntiles > 0) issue(0, kk0, kv0, vk0);
-  wait_vmem();
+  if (ntiles > 0) issue(0, kv0, vk0);
+  if (ntiles > 1) issue(32, kv1, vk1);
+  // loads complete in order: with tile 1 in flight, at most its LPT loads remain
+  if (ntiles > 1) wait_vmcnt<LPT>(); else wait_vmem();
   block_sync();
-  for (int t = 0; t < ntiles; t += 2) {
-    const int k0 = t * 32;
-    if (t + 1 < ntiles) issue(k0 + 32, kk1, kv1, vk1);
-    compute(k0, kk0, kv0, vk0);
-    wait_vmem();
-    block_sync();
-    if (t + 1 < ntiles) {
-      if (t + 2 < ntiles) issue(k0 + 64, kk0, kv0, vk0);
-      compute(k0 + 32, kk1, kv1, vk1);
-      wait_vmem();
-      block_sync();
+  for (int t = 0; t < ntiles; t += 3) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int tt = t + j;
+      if (tt < ntiles) {
+        if (tt + 2 < ntiles) issue((tt + 2) * 32, kvst(j + 2), vkst(j + 2));
+        compute(tt * 32, kvst(j), vkst(j));
+        // tile tt+1 has landed once only tile tt+2's loads (if any) are in flight
+        if (tt + 2 < ntiles) wait_vmcnt<LPT>(); else wait_vmem();
+        block_sync();
+      }
     }
   }
   store_rows<D>(a.dq + qo * D, r0, a.Sq, c, g, dqt, a.scale);
