@@ -729,20 +729,7 @@ __device__ __forceinline__ void sched_pairs() {
   }
 }
 
-// Interleave for one step of the key sweep: the S^T MFMAs of the next tile with the
-// exponentials and packing of this tile, then this tile's value MFMAs with its row sums.
-template <int DT, int D, int BN>
-__device__ __forceinline__ void interleave_step() {
-  constexpr int NKB = BN / 32;
-  constexpr int NQ = (D / 16) * NKB;          // S^T MFMAs
-  constexpr int NP = NKB * 2 * (D / 32);      // value MFMAs
-  constexpr int VE = NKB * (32 + 8);          // fma + exp per score, one convert per pair
-  constexpr int VS = NKB * (16 + 8);          // exact sum, consistent sum
-  sched_pairs<NQ, 0x8, 1, 0x2, (VE + NQ - 1) / NQ>();
-  sched_pairs<NP, 0x8, 1, 0x2, (VS + NP - 1) / NP>();
-}
-
-// The same for the bf16 main loop without a row maximum, whose tile step has two
+// Interleave for the bf16 main loop (no row maximum), whose tile step has two
 // scheduling regions (before and after the rare re-reference branch): the S^T MFMAs of
 // the next tile with the exponentials and the exact sum, then the value MFMAs with the
 // conversion and the consistent sum.
@@ -1360,17 +1347,6 @@ void attn_bwd_pre_kernel(BwdArgs a) {
 // dst[L]; rows past the buffer read as zeros).
 __device__ __forceinline__ void dma_floats(__amdgpu_buffer_rsrc_t rs, float* dst, int i0, int lane) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 4, (i0 + lane) * 4, 0, 0, 0);
-}
-
-// Four 16-byte chunks of the 32-float lse2 / D tile that lane (c, g) needs: the rows
-// 8*b + 4*g + 0..3 of its accumulator layout.
-__device__ __forceinline__ void load_row_terms(const float* t, int g, float (&x)[16]) {
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(t + 8 * b + 4 * g);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x[4 * b + r] = v[r];
-  }
 }
 
 __device__ __forceinline__ void pack_tile(const float (&x)[16], PTile<DT_BF16, 32>& pt) {
