@@ -1,4 +1,4 @@
-// Exact attention forward kernels for CDNA4 (gfx950).
+// Exact attention kernels for CDNA4 (gfx950): forward, split-KV merge, backward.
 //
 // One workgroup of four 64-lane wavefronts owns a tile of 128 query rows of one
 // (batch, head) and sweeps every visible key tile of that head, the sequence-level
@@ -30,7 +30,8 @@
 //
 // Split mode computes, for one chunk of the keys, the unnormalised state (m, l, u) of
 // the split-K section of "AI 大模型之 FlashAttention_02" and stores it in a
-// workspace; the merge kernel at the end of this file combines the chunks.
+// workspace; the merge kernel after the forward kernel combines the chunks.  The
+// backward kernels (dQ, dK, dV) close the file.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
