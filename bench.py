@@ -62,8 +62,12 @@ WORKLOADS = {
 
 
 def kernel_source_digest() -> str:
+    """Hash of the forward kernels' source: the kernel file up to its backward section (so
+    that a change to the backward kernels does not invalidate the forward's counters)."""
     with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        text = f.read()
+    cut = text.find(b"// " + b"=" * 66 + b" backward")
+    return hashlib.sha256(text[:cut] if cut > 0 else text).hexdigest()[:16]
 
 
 def read_traffic():
