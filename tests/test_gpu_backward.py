@@ -215,3 +215,28 @@ def test_backward_refuses_what_it_does_not_support():
         ea.attn_bwd(q.float(), k.float(), v.float(), o, l, dt)    # fp32: not supported
     with pytest.raises(ea.AttnError):
         ea.attn_bwd(q, k, v, o, l, dt, ws=torch.empty(16, dtype=torch.uint8, device="cuda"))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_at_the_c2_shape_two_heads(causal):
+    """B=8, H=32, S=2048, d=64 (the c2 workload's shape): the first and the last head
+    compared in full against the oracle (the others must be finite)."""
+    B, H, S, d = 8, 32, 2048, 64
+    inp, do = _inputs(B, H, S, S, d, seed=2)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    q, k, v = upload(inp)
+    o_t, l_t = ea.attn_fwd(q, k, v, scale=scale, causal=causal)
+    dt = torch.from_numpy(do).cuda()
+    grads = [_np(x) for x in ea.attn_bwd(q, k, v, o_t, l_t, dt, scale=scale, causal=causal)]
+    assert all(np.isfinite(x).all() for x in grads)
+    o_all, l_all = _np(o_t), _np(l_t)
+    for (b, h) in ((0, 0), (B - 1, H - 1)):
+        qh, kh, vh = (x[b, h] for x in (inp.q64, inp.k64, inp.v64))
+        o_ref, l_ref = oracle.attention(qh, kh, vh, scale, causal)
+        eo = float(np.abs(o_all[b, h] - o_ref).max())
+        el = float(np.abs(l_all[b, h] - l_ref).max())
+        one = si.AttentionInputs("bf16", 1, 1, S, S, d, 2, None, None, None,
+                                 qh[None, None], kh[None, None], vh[None, None])
+        _check_heads(one, do[b:b + 1, h:h + 1], scale, causal,
+                     tuple(x[b:b + 1, h:h + 1] for x in grads), extra_d=eo, extra_lse=el,
+                     label=f"bwd c2 shape head ({b},{h}) causal={causal}")
