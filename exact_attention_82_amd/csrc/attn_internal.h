@@ -157,8 +157,8 @@ inline BwdWorkspaceLayout bwd_workspace_layout(int64_t rows, int d) {
   return w;
 }
 
-// The backward kernels exist for bf16 with d = 64 or 128.
-constexpr bool bwd_supported(int dtype, int d) { return dtype == 1 && (d == 64 || d == 128); }
+// The backward kernels exist for bf16 with d = 64, 128 or 256.
+constexpr bool bwd_supported(int dtype, int d) { return dtype == 1 && (d == 64 || d == 128 || d == 256); }
 
 // Launchers (attn_kernels.hip).  Return a hipError_t value as int.
 int launch_fwd(const FwdArgs& a, void* stream);

@@ -1425,7 +1425,7 @@ __device__ __forceinline__ f32x16_t rows_product_reg(const uint8_t* xt, int xv,
 // complementary key tiles.
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(2, 2)))
+                          amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
 void attn_bwd_dkdv_kernel(BwdArgs a) {
   using Op = Traits<DT_BF16>::Op;
   using G = DmaGeo<DT_BF16, D, 32>;
@@ -1536,7 +1536,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(2, 2)))
+                          amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
 void attn_bwd_dq_kernel(BwdArgs a) {
   using Op = Traits<DT_BF16>::Op;
   using G = DmaGeo<DT_BF16, D, 32>;
@@ -1684,16 +1684,18 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   switch (a.d) {
     case 64: return int(launch_bwd_d<64>(a, s));
     case 128: return int(launch_bwd_d<128>(a, s));
+    case 256: return int(launch_bwd_d<256>(a, s));
   }
   return int(hipErrorInvalidValue);
 }
 
 const char* bwd_kernel_name(int d, int which) {
-  static const char* names[2][3] = {
+  static const char* names[3][3] = {
       {"attn_bwd_pre_d64", "attn_bwd_dkdv_bf16_d64_bn128_bm32", "attn_bwd_dq_bf16_d64_bm128_bn32"},
-      {"attn_bwd_pre_d128", "attn_bwd_dkdv_bf16_d128_bn128_bm32", "attn_bwd_dq_bf16_d128_bm128_bn32"}};
-  if ((d != 64 && d != 128) || which < 0 || which > 2) return "";
-  return names[d == 64 ? 0 : 1][which];
+      {"attn_bwd_pre_d128", "attn_bwd_dkdv_bf16_d128_bn128_bm32", "attn_bwd_dq_bf16_d128_bm128_bn32"},
+      {"attn_bwd_pre_d256", "attn_bwd_dkdv_bf16_d256_bn128_bm32", "attn_bwd_dq_bf16_d256_bm128_bn32"}};
+  if ((d != 64 && d != 128 && d != 256) || which < 0 || which > 2) return "";
+  return names[d == 64 ? 0 : d == 128 ? 1 : 2][which];
 }
 
 int device_cu_count() {

@@ -160,7 +160,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int d);
  *   dq, dk, dv   device pointers, fp32 outputs [B,H,Sq,d], [B,H,Sk,d], [B,H,Sk,d]
  *   ws, ws_bytes device workspace of at least attn_bwd_workspace_bytes(B, H, Sq, d)
  *   scale, causal as for attn_fwd
- * Supported: dtype ATTN_BF16 with d = 64 or 128 (else ATTN_ERR_UNSUPPORTED).  All
+ * Supported: dtype ATTN_BF16 with d = 64, 128 or 256 (else ATTN_ERR_UNSUPPORTED).  All
  * pointers 16-byte aligned, buffers contiguous and not overlapping.  dO is used rounded
  * to bf16, and P and dS are rounded to bf16 as operands of the products (fp32
  * accumulation).  Asynchronous on `stream` (three launches); the library allocates

@@ -120,6 +120,8 @@ def _oracle_fwd(inp, scale, causal):
     (1, 1, 1000, 1000, 128, False, 0.0),
     (1, 1, 1, 5, 64, False, 0.0),
     (1, 1, 33, 1, 128, True, 0.0),
+    (1, 2, 300, 300, 256, False, 0.0),
+    (2, 1, 257, 190, 256, True, 0.0),
 ])
 def test_backward_matches_oracle(B, H, Sq, Sk, d, causal, hot):
     inp, do = _inputs(B, H, Sq, Sk, d, seed=31 + Sq + d, hot=hot)

@@ -147,7 +147,7 @@ def test_backward_refuses_bad_arguments_and_lays_out_its_workspace(lib):
                             causal, dtype, None)
     assert bwd(q=None) == 1 and bwd(dout=None) == 1 and bwd(dq=None) == 1 and bwd(ws=None) == 1
     assert bwd(nb=need - 1) == 5
-    assert bwd(d=256) == 4          # the backward covers d = 64 and 128
+    assert bwd(d=96) == 4           # the backward covers d = 64, 128 and 256
     assert bwd(dtype=0) == 4 and bwd(dtype=2) == 4   # bf16 only
     assert bwd(dq=DQ + 4) == 3 and bwd(ws=W + 8) == 3
     assert bwd(causal=3) == 7 and bwd(scale=-1.0) == 7
