@@ -28,7 +28,8 @@ B=1,H=2,S=128,d=64) reports microseconds; c2 and the 36 c4 cases (d in 64/128/25
 against min(bf16 MFMA peak, intensity x 8 TB/s); c5 (fp8 B=1,H=8,Sq=128,Sk=32768,d=128)
 times attn_fwd_splitkv and attn_merge apart for n = 1, 4, 16 and reports the algorithmic
 bytes (Q, K, V read once, O and lse written once) per second against 8 TB/s.  bwd times
-attn_bwd (three launches: prologue, dK/dV, dQ) at the c3 and c2 shapes with inputs
+attn_bwd (three launches: prologue, dK/dV, dQ) at the c3 and c2 shapes and at B=1, H=16,
+S=2048, d=256, with inputs
 resident (repeated calls), counting 10*B*H*Sq*Sk*d FLOPs (2.5x the forward's: the five
 products S, dP, dV, dK, dQ; half causal) against the bf16 MFMA peak, and times the fp64
 oracle's backward on one head beside it.
@@ -275,7 +276,7 @@ def sweep(name: str, reps: int, warmup: int):
         return
     if name == "bwd":
         import oracle
-        for (B, H, S, d, seed) in ((1, 8, 8192, 128, 3), (8, 32, 2048, 64, 2)):
+        for (B, H, S, d, seed) in ((1, 8, 8192, 128, 3), (8, 32, 2048, 64, 2), (1, 16, 2048, 256, 421)):
             inp = si.make_attention_inputs(B, H, S, S, d, seed=seed, dtype="bf16")
             q, k, v = to_dev(inp)
             rng = np.random.default_rng(seed + 1000)
