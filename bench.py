@@ -282,7 +282,7 @@ def sweep(name: str, reps: int, warmup: int):
             rng = np.random.default_rng(seed + 1000)
             do = torch.from_numpy(rng.standard_normal((B, H, S, d), dtype=np.float32)).to(dev)
             scale = float(np.float32(1.0 / np.sqrt(d)))
-            ws = torch.empty(ea.attn_bwd_workspace_bytes(B, H, S, d), dtype=torch.uint8, device=dev)
+            ws = torch.empty(ea.attn_bwd_workspace_bytes(B, H, S, S, d, True), dtype=torch.uint8, device=dev)
             dq = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
             dk, dv = torch.empty_like(dq), torch.empty_like(dq)
             for causal in (False, True):

@@ -122,8 +122,8 @@ def attn_merge(ws, num_splits, B, H, Sq, d, out=None, lse=None, stream=None):
     return out, lse
 
 
-def attn_bwd_workspace_bytes(B, H, Sq, d) -> int:
-    return int(_lib.load().attn_bwd_workspace_bytes(B, H, Sq, d))
+def attn_bwd_workspace_bytes(B, H, Sq, Sk, d, causal=False) -> int:
+    return int(_lib.load().attn_bwd_workspace_bytes(B, H, Sq, Sk, d, int(causal)))
 
 
 def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None,
@@ -144,7 +144,7 @@ def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, 
     if dv is None:
         dv = torch.empty((B, H, Sk, d), dtype=torch.float32, device=dev)
     if ws is None:
-        ws = torch.empty(max(attn_bwd_workspace_bytes(B, H, Sq, d), 16), dtype=torch.uint8,
+        ws = torch.empty(max(attn_bwd_workspace_bytes(B, H, Sq, Sk, d, causal), 16), dtype=torch.uint8,
                          device=dev)
     st = _lib.load().attn_bwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(o),
                               ctypes_ptr(dout), ctypes_ptr(lse), ctypes_ptr(dq), ctypes_ptr(dk),

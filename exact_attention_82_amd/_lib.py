@@ -29,7 +29,7 @@ SIGNATURES = {
     "attn_block_n": (_i, [_i, _i]),
     "attn_num_workgroups": (ctypes.c_int64, [_i, _i, _i, _i, _i, _i, _i]),
     "attn_kernel_name": (ctypes.c_char_p, [_i, _i, _i, _i, _i, _i, _i]),
-    "attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _i,
                       _f, _i, _i, _vp]),
     "attn_bwd_kernel_name": (ctypes.c_char_p, [_i, _i, _i]),

@@ -155,11 +155,11 @@ attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o
   return launched(attn::launch_merge(a, stream));
 }
 
-size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int d) {
-  if (B < 1 || H < 1 || Sq < 1 || !supported_d(d)) return 0;
-  const int64_t rows = int64_t(B) * H * Sq;
-  if (rows * d >= kMaxIndex) return 0;
-  return attn::bwd_workspace_layout(rows, d).total;
+size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || !supported_d(d) || (causal != 0 && causal != 1)) return 0;
+  const int64_t bh = int64_t(B) * H;
+  if (bh * Sq * d >= kMaxIndex || bh * Sk * d >= kMaxIndex) return 0;
+  return attn::bwd_workspace_layout(bh, Sq, Sk, d, causal).total;
 }
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o,
@@ -176,8 +176,8 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o
   if ((causal != 0 && causal != 1) || !positive_finite(scale)) return ATTN_ERR_ARG;
   const float sl2 = static_cast<float>(double(scale) * kLog2e);
   if (!positive_finite(sl2)) return ATTN_ERR_ARG;
-  const int64_t rows = int64_t(B) * H * Sq;
-  const attn::BwdWorkspaceLayout w = attn::bwd_workspace_layout(rows, d);
+  const int64_t bh = int64_t(B) * H;
+  const attn::BwdWorkspaceLayout w = attn::bwd_workspace_layout(bh, Sq, Sk, d, causal);
   if (ws_bytes < w.total) return ATTN_ERR_WORKSPACE;
 
   char* base = static_cast<char*>(ws);
@@ -187,15 +187,22 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o
   a.do16 = reinterpret_cast<uint16_t*>(base + w.do_off);
   a.dsum = reinterpret_cast<float*>(base + w.dsum_off);
   a.lse2 = reinterpret_cast<float*>(base + w.lse2_off);
+  a.pdk = reinterpret_cast<float*>(base + w.pdk_off);
+  a.pdv = reinterpret_cast<float*>(base + w.pdv_off);
   a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = sl2;
+  // Split the long causal key tiles only when the whole dK/dV grid is resident at once
+  // (two workgroups per CU); larger grids already balance as workgroups finish.
+  const int64_t nkt = (Sk + attn::kBlockM - 1) / attn::kBlockM;
+  const int cus = attn::device_cu_count();
+  a.long_tiles = (cus > 0 && bh * nkt <= 2 * int64_t(cus)) ? attn::bwd_long_tiles(Sq, Sk, causal) : 0;
   return launched(attn::launch_bwd(a, stream));
 }
 
 const char* attn_bwd_kernel_name(int d, attn_dtype dtype, int which) {
-  if (!attn::bwd_supported(dtype, d) || which < 0 || which > 2) return "unsupported";
+  if (!attn::bwd_supported(dtype, d) || which < 0 || which > 3) return "unsupported";
   return attn::bwd_kernel_name(d, which);
 }
 

@@ -141,19 +141,46 @@ struct BwdArgs {
   int causal;
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
+  int long_tiles;    // key tiles 0..long_tiles-1 are swept in two halves (causal, small grids)
+  float* pdk;        // workspace [B*H][long_tiles*128][d]: second halves' dK
+  float* pdv;        // same for dV
 };
+
+// Query tiles (of 32 rows) the dK/dV sweep of 128-key tile kt visits: rows from
+// kt*128 - (Sk - Sq) on (causal), rounded down to a tile.
+inline int bwd_query_tiles(int Sq, int Sk, int kt, int causal) {
+  int beg = causal ? kt * 128 - (Sk - Sq) : 0;
+  beg = beg > 0 ? (beg / 32) * 32 : 0;
+  return beg < Sq ? (Sq - beg + 31) / 32 : 0;
+}
+
+// Causal key tiles whose sweep covers more than half of the query tiles (a prefix: the
+// sweeps shrink with kt).  When a grid is resident all at once, these are swept in two
+// halves by two workgroups so that no workgroup runs much longer than the others.
+inline int bwd_long_tiles(int Sq, int Sk, int causal) {
+  if (!causal) return 0;
+  const int nq = (Sq + 31) / 32, nkt = (Sk + 127) / 128;
+  int n = 0;
+  while (n < nkt && bwd_query_tiles(Sq, Sk, n, 1) > (nq + 1) / 2) ++n;
+  return n;
+}
 
 struct BwdWorkspaceLayout {
-  size_t do_off, dsum_off, lse2_off, total;
+  size_t do_off, dsum_off, lse2_off, pdk_off, pdv_off, total;
 };
 
-inline BwdWorkspaceLayout bwd_workspace_layout(int64_t rows, int d) {
+inline BwdWorkspaceLayout bwd_workspace_layout(int64_t bh, int Sq, int Sk, int d, int causal) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t rows = size_t(bh) * size_t(Sq);
+  const int lt = bwd_long_tiles(Sq, Sk, causal);
+  const size_t prow = size_t(bh) * size_t(lt) * 128;
   BwdWorkspaceLayout w;
   w.do_off = 0;
-  w.dsum_off = up(size_t(rows) * size_t(d) * 2);
-  w.lse2_off = w.dsum_off + up(size_t(rows) * sizeof(float));
-  w.total = w.lse2_off + up(size_t(rows) * sizeof(float));
+  w.dsum_off = up(rows * size_t(d) * 2);
+  w.lse2_off = w.dsum_off + up(rows * sizeof(float));
+  w.pdk_off = w.lse2_off + up(rows * sizeof(float));
+  w.pdv_off = w.pdk_off + up(prow * size_t(d) * sizeof(float));
+  w.total = w.pdv_off + up(prow * size_t(d) * sizeof(float));
   return w;
 }
 
@@ -164,7 +191,7 @@ constexpr bool bwd_supported(int dtype, int d) { return dtype == 1 && (d == 64 |
 int launch_fwd(const FwdArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_bwd(const BwdArgs& a, void* stream);
-const char* bwd_kernel_name(int d, int which);  // which: 0 prologue, 1 dK/dV, 2 dQ
+const char* bwd_kernel_name(int d, int which);  // which: 0 prologue, 1 dK/dV, 2 dQ, 3 combine
 // Compute units of the current device (cached per device), or 0 if unknown.
 int device_cu_count();
 const char* fwd_kernel_name(int dtype, int d, int split_mode, int sched);

@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_internal.h"
@@ -1436,13 +1437,13 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, g = lane >> 5;
   const int BH = a.B * a.H;
-  const int nkt = ceil_div_i(a.Sk, kBlockM);
   const int bh = blockIdx.x % BH;
-  int kt = blockIdx.x / BH;
-  if (a.causal) {
-    const int half = (nkt + 1) / 2;
-    kt = kt < half ? kt : nkt - 1 - (kt - half);
-  }
+  // Work items, longest sweeps first: the two halves of each long key tile, then the
+  // other key tiles in order.
+  const int item = blockIdx.x / BH;
+  const int L = a.long_tiles;
+  const int kt = item < 2 * L ? item / 2 : item - L;
+  const int part = item < 2 * L ? item % 2 : -1;  // -1: the whole sweep
   const int kw0 = kt * kBlockM + wave * 32;  // first key of this wavefront
   const int key = kw0 + c;                   // this lane's key
   const int off = a.Sk - a.Sq;
@@ -1476,8 +1477,13 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(256))) float ls0[64], ds0[64], ls1[64], ds1[64];
   const uint8_t* vmine = wave == 0 ? vb0 : wave == 1 ? vb1 : wave == 2 ? vb2 : vb3;
 
-  const int ibeg = a.causal ? (max(0, kt * kBlockM - off) / 32) * 32 : 0;
-  const int ntiles = ibeg < a.Sq ? ceil_div_i(a.Sq - ibeg, 32) : 0;
+  int ibeg = a.causal ? (max(0, kt * kBlockM - off) / 32) * 32 : 0;
+  int ntiles = ibeg < a.Sq ? ceil_div_i(a.Sq - ibeg, 32) : 0;
+  if (part >= 0) {  // first or second half of the query tiles
+    const int h = (ntiles + 1) / 2;
+    if (part == 1) ibeg += h * 32;
+    ntiles = part == 0 ? h : ntiles - h;
+  }
 
   auto issue = [&](int i0, uint8_t* qs, uint8_t* os, float* ls, float* ds) __attribute__((always_inline)) {
     pipe.issue_v(rq, i0, qs);
@@ -1530,8 +1536,31 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       block_sync();
     }
   }
-  store_rows<D>(a.dk + ko * D, kw0, a.Sk, c, g, dkt, a.scale);
-  store_rows<D>(a.dv + ko * D, kw0, a.Sk, c, g, dvt, 1.0f);
+  if (part == 1) {  // second half: to the workspace, added by attn_bwd_combine_kernel
+    const size_t po = size_t(bh) * size_t(L) * kBlockM;
+    store_rows<D>(a.pdk + po * D, kw0, a.Sk, c, g, dkt, a.scale);
+    store_rows<D>(a.pdv + po * D, kw0, a.Sk, c, g, dvt, 1.0f);
+  } else {
+    store_rows<D>(a.dk + ko * D, kw0, a.Sk, c, g, dkt, a.scale);
+    store_rows<D>(a.dv + ko * D, kw0, a.Sk, c, g, dvt, 1.0f);
+  }
+}
+
+// dK, dV of the split key tiles: first half (already in place) + second half (workspace),
+// in that order, so the sum does not depend on timing.
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void attn_bwd_combine_kernel(BwdArgs a) {
+  const int rows = min(a.Sk, a.long_tiles * kBlockM);  // per (batch, head)
+  const int64_t n4 = int64_t(a.B) * a.H * rows * (D / 4);
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / (D / 4), col = (i % (D / 4)) * 4;
+    const int64_t bh = r / rows, kr = r % rows;
+    const size_t o = size_t(bh * a.Sk + kr) * D + col;
+    const size_t w = size_t(bh * int64_t(a.long_tiles) * kBlockM + kr) * D + col;
+    *reinterpret_cast<f32x4_t*>(a.dk + o) += *reinterpret_cast<const f32x4_t*>(a.pdk + w);
+    *reinterpret_cast<f32x4_t*>(a.dv + o) += *reinterpret_cast<const f32x4_t*>(a.pdv + w);
+  }
 }
 
 template <int D>
@@ -1649,8 +1678,13 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   constexpr int RPB = 256 / (D / 4);
   const int64_t pre = (rows + RPB - 1) / RPB;
   hipLaunchKernelGGL(attn_bwd_pre_kernel<D>, dim3(unsigned(pre < 65536 ? pre : 65536)), dim3(256), 0, s, a);
-  const int64_t nkv = int64_t(a.B) * a.H * ((a.Sk + kBlockM - 1) / kBlockM);
+  const int64_t nkv = int64_t(a.B) * a.H * ((a.Sk + kBlockM - 1) / kBlockM + a.long_tiles);
   if (nkv > 0) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(unsigned(nkv)), dim3(kThreads), 0, s, a);
+  if (a.long_tiles > 0) {
+    const int64_t n4 = int64_t(a.B) * a.H * std::min<int64_t>(a.Sk, int64_t(a.long_tiles) * kBlockM) * (D / 4);
+    const int64_t nb = (n4 + 255) / 256;
+    hipLaunchKernelGGL(attn_bwd_combine_kernel<D>, dim3(unsigned(nb < 65536 ? nb : 65536)), dim3(256), 0, s, a);
+  }
   const int64_t nq = int64_t(a.B) * a.H * ((a.Sq + kBlockM - 1) / kBlockM);
   if (nq > 0) hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(unsigned(nq)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
@@ -1690,11 +1724,11 @@ int launch_bwd(const BwdArgs& a, void* stream) {
 }
 
 const char* bwd_kernel_name(int d, int which) {
-  static const char* names[3][3] = {
-      {"attn_bwd_pre_d64", "attn_bwd_dkdv_bf16_d64_bn128_bm32", "attn_bwd_dq_bf16_d64_bm128_bn32"},
-      {"attn_bwd_pre_d128", "attn_bwd_dkdv_bf16_d128_bn128_bm32", "attn_bwd_dq_bf16_d128_bm128_bn32"},
-      {"attn_bwd_pre_d256", "attn_bwd_dkdv_bf16_d256_bn128_bm32", "attn_bwd_dq_bf16_d256_bm128_bn32"}};
-  if ((d != 64 && d != 128 && d != 256) || which < 0 || which > 2) return "";
+  static const char* names[3][4] = {
+      {"attn_bwd_pre_d64", "attn_bwd_dkdv_bf16_d64_bn128_bm32", "attn_bwd_dq_bf16_d64_bm128_bn32", "attn_bwd_combine_d64"},
+      {"attn_bwd_pre_d128", "attn_bwd_dkdv_bf16_d128_bn128_bm32", "attn_bwd_dq_bf16_d128_bm128_bn32", "attn_bwd_combine_d128"},
+      {"attn_bwd_pre_d256", "attn_bwd_dkdv_bf16_d256_bn128_bm32", "attn_bwd_dq_bf16_d256_bm128_bn32", "attn_bwd_combine_d256"}};
+  if ((d != 64 && d != 128 && d != 256) || which < 0 || which > 3) return "";
   return names[d == 64 ? 0 : d == 128 ? 1 : 2][which];
 }
 

@@ -136,9 +136,11 @@ attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o
  * attn_bwd_workspace_bytes -- bytes of the workspace attn_bwd needs for this shape, or 0
  * if an argument is out of range.  Layout (each section at a multiple of 256 bytes from
  * the base), R = B*H*Sq rows: dO rounded to bf16 [R][d], D = sum_d dO*O [R] (fp32), lse
- * in log2 units [R] (fp32).  Contents are scratch between calls.
+ * in log2 units [R] (fp32); causal only, the second-half partial dK and dV [B*H][L*128][d]
+ * (fp32) of the L long key tiles (those whose causal sweep covers more than half of the
+ * query rows), which attn_bwd may split between two workgroups.  Contents are scratch.
  */
-size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int d);
+size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal);
 
 /*
  * attn_bwd -- gradients of the forward above with respect to Q, K and V.
@@ -158,21 +160,21 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int d);
  *   o, dout      device pointers, fp32 [B,H,Sq,d]: forward output and upstream gradient
  *   lse          device pointer, fp32 [B,H,Sq]: forward log-sum-exp (natural log)
  *   dq, dk, dv   device pointers, fp32 outputs [B,H,Sq,d], [B,H,Sk,d], [B,H,Sk,d]
- *   ws, ws_bytes device workspace of at least attn_bwd_workspace_bytes(B, H, Sq, d)
+ *   ws, ws_bytes device workspace of at least attn_bwd_workspace_bytes(B, H, Sq, Sk, d, causal)
  *   scale, causal as for attn_fwd
  * Supported: dtype ATTN_BF16 with d = 64, 128 or 256 (else ATTN_ERR_UNSUPPORTED).  All
  * pointers 16-byte aligned, buffers contiguous and not overlapping.  dO is used rounded
  * to bf16, and P and dS are rounded to bf16 as operands of the products (fp32
- * accumulation).  Asynchronous on `stream` (three launches); the library allocates
- * nothing.  Errors are returned before any launch.
+ * accumulation).  Asynchronous on `stream` (three launches, four when long causal key
+ * tiles are split); the library allocates nothing.  Errors are returned before any launch.
  */
 attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o,
                      const float* dout, const float* lse, float* dq, float* dk, float* dv,
                      void* ws, size_t ws_bytes, int B, int H, int Sq, int Sk, int d,
                      float scale, int causal, attn_dtype dtype, void* stream);
 
-/* Name of a kernel attn_bwd launches: which = 0 prologue, 1 dK/dV, 2 dQ ("unsupported"
- * if none). */
+/* Name of a kernel attn_bwd launches: which = 0 prologue, 1 dK/dV, 2 dQ, 3 the combine
+ * pass of split key tiles ("unsupported" if none). */
 const char* attn_bwd_kernel_name(int d, attn_dtype dtype, int which);
 
 /*

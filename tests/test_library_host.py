@@ -137,9 +137,15 @@ def test_backward_refuses_bad_arguments_and_lays_out_its_workspace(lib):
     B, H, Sq, Sk, d = 1, 2, 16, 24, 128
     rows = B * H * Sq
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    need = lib.attn_bwd_workspace_bytes(B, H, Sq, d)
+    need = lib.attn_bwd_workspace_bytes(B, H, Sq, Sk, d, 0)
     assert need == up(rows * d * 2) + up(rows * 4) + up(rows * 4)
-    assert lib.attn_bwd_workspace_bytes(B, H, Sq, 100) == 0
+    assert lib.attn_bwd_workspace_bytes(B, H, Sq, Sk, 100, 0) == 0
+    assert lib.attn_bwd_workspace_bytes(B, H, Sq, Sk, d, 2) == 0
+    # causal, Sq = Sk = 700: key tiles 0-2 sweep more than half of the 22 query tiles
+    # (22, 18, 14 > 11), so the workspace also holds their second-half dK and dV
+    base = up(2 * 700 * d * 2) + 2 * up(2 * 700 * 4)
+    assert lib.attn_bwd_workspace_bytes(1, 2, 700, 700, d, 1) == base + 2 * up(2 * 3 * 128 * d * 4)
+    assert lib.attn_bwd_workspace_bytes(1, 2, 700, 700, d, 0) == base
     DO, DQ, DK, DV, W = 0x60000, 0x70000, 0x80000, 0x90000, 0xA0000
 
     def bwd(q=Q, dout=DO, dq=DQ, ws=W, nb=need, d=d, dtype=1, causal=0, scale=0.125):
