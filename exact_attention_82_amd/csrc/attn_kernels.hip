@@ -35,7 +35,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <algorithm>
 #include <type_traits>
 
 #include "attn_internal.h"
@@ -1681,7 +1680,8 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int64_t nkv = int64_t(a.B) * a.H * ((a.Sk + kBlockM - 1) / kBlockM + a.long_tiles);
   if (nkv > 0) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(unsigned(nkv)), dim3(kThreads), 0, s, a);
   if (a.long_tiles > 0) {
-    const int64_t n4 = int64_t(a.B) * a.H * std::min<int64_t>(a.Sk, int64_t(a.long_tiles) * kBlockM) * (D / 4);
+    const int64_t zr = int64_t(a.long_tiles) * kBlockM < a.Sk ? int64_t(a.long_tiles) * kBlockM : a.Sk;
+    const int64_t n4 = int64_t(a.B) * a.H * zr * (D / 4);
     const int64_t nb = (n4 + 255) / 256;
     hipLaunchKernelGGL(attn_bwd_combine_kernel<D>, dim3(unsigned(nb < 65536 ? nb : 65536)), dim3(256), 0, s, a);
   }
