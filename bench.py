@@ -505,6 +505,7 @@ def main():
                 "median_us": round(float(np.median(per_mode_ms[c])) * 1e3, 2),
                 "p10_us": round(float(np.percentile(per_mode_ms[c], 10)) * 1e3, 2),
                 "p90_us": round(float(np.percentile(per_mode_ms[c], 90)) * 1e3, 2),
+                "min_us": round(float(np.min(per_mode_ms[c])) * 1e3, 2),
                 "pct_bf16_peak": round(100.0 * flops[c] / (np.median(per_mode_ms[c]) * 1e-3)
                                        / 1e12 / PEAK_BF16_TFLOPS, 2),
             } for c in modes
