@@ -934,7 +934,9 @@ void attn_fwd_kernel(FwdArgs p) {
         }
       }
     }
-    wait_vmem();
+    // Key tiles 0 and 1 and value tile 0 are what the first iteration reads; the loads
+    // complete in order, so the later NS-2 tiles' worth may stay in flight.
+    P::template wait_loads<NS - 2>();
     block_sync();
     f32x16_t sa[NKB], sb[NKB];
     if (ntiles > 0 && active(kbeg)) pipe.qk(sa, kst(0), qop);
