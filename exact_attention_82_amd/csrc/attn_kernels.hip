@@ -1497,6 +1497,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     const f32x16_t st = rows_product_reg<D>(qs, xv, kop);              // S  [query][key]
     const f32x16_t dp = rows_product_lds<D>(os, xv, vmine, ln.kx);     // dP [query][key]
     float pv[16], sv[16];
+    // every (query, key) pair of this wavefront's block visible: no per-element test
+    const bool full = i0 + 32 <= a.Sq && kw0 + 32 <= a.Sk && (!a.causal || kw0 + 31 <= i0 + off);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(ls + 8 * b + 4 * g);
@@ -1505,7 +1507,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int e = 4 * b + r;
         const int i = i0 + 8 * b + 4 * g + r;
-        const bool vis = i < a.Sq && key < a.Sk && (!a.causal || key <= i + off);
+        const bool vis = full || (i < a.Sq && key < a.Sk && (!a.causal || key <= i + off));
         const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[e], sl2, -l4[r])) : 0.0f;
         pv[e] = p;
         sv[e] = p * (dp[e] - d4[r]);
@@ -1640,10 +1642,12 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     f32x16_t dpt[1];
     qk_dma<DT_BF16, D, 32>(dpt, vk, dop, ln);              // dP^T [key][query]
     float sv[16];
+    // every (key, query) pair of this wavefront's block visible: no per-element test
+    const bool full = k0 + 32 <= kend && r0 + 32 <= a.Sq && (!a.causal || k0 + 31 <= r0 + off);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int kj = k0 + 8 * (e >> 2) + 4 * g + (e & 3);
-      const bool vis = kj < kend && row < a.Sq && (!a.causal || kj <= row + off);
+      const bool vis = full || (kj < kend && row < a.Sq && (!a.causal || kj <= row + off));
       const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[e], sl2, -l2)) : 0.0f;
       sv[e] = p * (dpt[0][e] - dd);
     }
