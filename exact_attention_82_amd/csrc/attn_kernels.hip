@@ -179,6 +179,36 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint8_t* sta
   }
 }
 
+// A (batch, head) slice of K or V: base address and size in bytes.  Forward tile
+// loads address it through a buffer resource rebased to the tile's first row (scalar
+// arithmetic only), so the per-lane offsets stay loop-invariant and the range check,
+// which returns zeros past the slice, stays exact.
+struct Slice {
+  const uint8_t* base;
+  uint32_t bytes;
+};
+
+template <int DT, int D, int BN, bool VALUE, int NW = kWaves>
+__device__ __forceinline__ void dma_tile_at(const Slice& sl, uint8_t* stage, int k0, int wave, int lane) {
+  using G = DmaGeo<DT, D, BN>;
+  constexpr int NI = G::TILE / 1024 / NW;
+  static_assert(NI >= 1 && G::TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads");
+  const uint32_t off = uint32_t(k0) * G::ROWB;
+  // signed max, not a saturating subtract: the latter has no scalar form, and a buffer
+  // resource computed in vector registers costs a loop per load (both values < 2^31)
+  const int left = __builtin_amdgcn_readfirstlane(max(int(sl.bytes) - int(off), 0));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl.base + off, uint32_t(left));
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int blk = wave * NI + j;
+    const int L = blk * 64 + lane;
+    const int row = L / G::CPR, chp = L % G::CPR;
+    const int ch = chp ^ (VALUE ? swz_v<DT, G::ROWB>(row) : swz_k<G::ROWB>(row));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + blk * 1024), 16,
+                                             row * G::ROWB + ch * 16, 0, 0, 0);
+  }
+}
+
 // Per-lane LDS offsets (relative to a stage) used by the operand reads.
 template <int DT, int D, int BN> struct DmaLane {
   using G = DmaGeo<DT, D, BN>;
@@ -583,7 +613,7 @@ __device__ __forceinline__ float softmax_exp_ref(const f32x16_t (&s)[BN / 32], f
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       p[b][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][j], sl2, -m_ref));
-      ls += p[b][j];
+      ls = (b == 0 && j == 0) ? p[b][j] : ls + p[b][j];
     }
   return ls;
 }
@@ -674,6 +704,12 @@ template <int DT, int D, int BN, int NW> struct Pipe<DT, D, BN, NW, true> {
   __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rs, int k0, uint8_t* dst) {
     dma_tile<DT, D, BN, true, NW>(rs, dst, k0, wave, lane);
   }
+  __device__ __forceinline__ void issue_k(const Slice& sl, int k0, uint8_t* dst) {
+    dma_tile_at<DT, D, BN, false, NW>(sl, dst, k0, wave, lane);
+  }
+  __device__ __forceinline__ void issue_v(const Slice& sl, int k0, uint8_t* dst) {
+    dma_tile_at<DT, D, BN, true, NW>(sl, dst, k0, wave, lane);
+  }
   __device__ __forceinline__ void commit_k(uint8_t*, int) {}
   __device__ __forceinline__ void commit_v(uint8_t*, int) {}
   __device__ __forceinline__ void qk(f32x16_t (&s)[BN / 32], const uint8_t* kt, const Op (&qop)[KSTEPS]) {
@@ -703,6 +739,12 @@ template <int DT, int D, int BN, int NW> struct Pipe<DT, D, BN, NW, false> {
   __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rs, int k0, uint8_t*) {
     st_load<D, BN>(rv, rs, k0, threadIdx.x);
   }
+  __device__ __forceinline__ void issue_k(const Slice& sl, int k0, uint8_t*) {
+    st_load<D, BN>(rk, make_rsrc(sl.base, sl.bytes), k0, threadIdx.x);
+  }
+  __device__ __forceinline__ void issue_v(const Slice& sl, int k0, uint8_t*) {
+    st_load<D, BN>(rv, make_rsrc(sl.base, sl.bytes), k0, threadIdx.x);
+  }
   __device__ __forceinline__ void commit_k(uint8_t* dst, int tid) { st_store<D, BN, G::K_STRIDE>(rk, dst, tid); }
   __device__ __forceinline__ void commit_v(uint8_t* dst, int tid) { st_store<D, BN, G::V_STRIDE>(rv, dst, tid); }
   __device__ __forceinline__ void qk(f32x16_t (&s)[BN / 32], const uint8_t* kt, const float (&qop)[KSTEPS]) {
@@ -730,23 +772,18 @@ __device__ __forceinline__ void sched_pairs() {
   }
 }
 
-// Interleave for the bf16 main loop (no row maximum), whose tile step has two
-// scheduling regions (before and after the rare re-reference branch): the S^T MFMAs of
-// the next tile with the exponentials and the exact sum, then the value MFMAs with the
-// conversion and the consistent sum.
+// Interleave for the bf16 main loop (no row maximum): each of the iteration's MFMAs
+// (S^T of tile t+2, then P(t) V(t)) is followed by a share of the VALU work on tile
+// t+1 -- exponentials, row sum, bf16 packing and the sum of the packed values -- none
+// of which the MFMAs depend on.
 template <int D, int BN>
-__device__ __forceinline__ void interleave_exp() {
+__device__ __forceinline__ void interleave_deferred() {
   constexpr int NKB = BN / 32;
-  constexpr int NQ = (D / 16) * NKB;
-  constexpr int VE = NKB * 48;                // fma + exp + add per score
-  sched_pairs<NQ, 0x8, 1, 0x2, (VE + NQ - 1) / NQ>();
-}
-template <int D, int BN>
-__device__ __forceinline__ void interleave_pv() {
-  constexpr int NKB = BN / 32;
-  constexpr int NP = NKB * 2 * (D / 32);
-  constexpr int VS = NKB * 16;                // converts and dot products
-  sched_pairs<NP, 0x8, 1, 0x2, (VS + NP - 1) / NP>();
+  constexpr int NM = (D / 16) * NKB + NKB * 2 * (D / 32);  // MFMAs per iteration
+  constexpr int NV = NKB * (48 + 16);                       // VALU per iteration
+  constexpr int NR = NKB * (D / 16) + NKB * 2 * (D / 32) * 2;  // LDS operand reads
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+  sched_pairs<NM, 0x8, 1, 0x2, (NV + NM - 1) / NM>();
 }
 
 // ================================================================== forward kernel
@@ -837,10 +874,8 @@ void attn_fwd_kernel(FwdArgs p) {
   const size_t kv_base = size_t(bh) * p.Sk * D;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint8_t*>(p.q) + q_base * EB,
                                               uint32_t(p.Sq) * D * EB);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + kv_base * EB,
-                                              uint32_t(p.Sk) * D * EB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + kv_base * EB,
-                                              uint32_t(p.Sk) * D * EB);
+  const Slice rk{reinterpret_cast<const uint8_t*>(p.k) + kv_base * EB, uint32_t(p.Sk) * D * EB};
+  const Slice rv{reinterpret_cast<const uint8_t*>(p.v) + kv_base * EB, uint32_t(p.Sk) * D * EB};
 
   // ---- per-wavefront state of the query tile being swept
   int q0 = 0, r0 = 0, row = 0, wave_last = 0;
@@ -918,6 +953,134 @@ void attn_fwd_kernel(FwdArgs p) {
       return (k0 + BN > kend) || (p.causal && (k0 + BN - 1 > r0 + off));
     };
 
+    if constexpr (P::kRegOps) {
+      // ---- deferred pipeline (bf16, d <= 128).  Iteration t computes S^T of key tile
+      // t+2, adds P(t) V(t) with the probabilities packed in iteration t-1, and turns
+      // the scores of tile t+1 into P(t+1): none of the iteration's MFMAs waits for
+      // its own exponentials, so the two interleave freely.  Tile j's keys and values
+      // live in stage j % 4; iteration t requests key tile t+5 (into the stage of key
+      // tile t+1, read in iteration t-1) and value tile t+3 (into the stage of value
+      // tile t-1).  In every iteration the newest two iterations' loads may stay in
+      // flight: loads complete in order, so key tile t+3 and value tile t+1 (needed
+      // next) have then landed.
+      static_assert(NS == 4 && U == 4, "the stage plan assumes a four-stage ring");
+      f32x16_t sa[NKB], sb[NKB];
+      PTile<DT, BN> pa, pb;
+      if (ntiles > 0) {
+        pipe.issue_k(rk, kbeg + 0 * BN, kst(0));
+        pipe.issue_k(rk, kbeg + 1 * BN, kst(1));
+        pipe.issue_k(rk, kbeg + 2 * BN, kst(2));
+        pipe.issue_v(rv, kbeg + 0 * BN, vst(0));
+        pipe.issue_k(rk, kbeg + 3 * BN, kst(3));
+        pipe.issue_v(rv, kbeg + 1 * BN, vst(1));
+      }
+      P::template wait_loads<2>();  // key tiles 0 and 1
+      block_sync();
+      const bool act0 = ntiles > 0 && active(kbeg);
+      if (act0) pipe.qk(sa, kst(0), qop);
+      if (ntiles > 1 && active(kbeg + BN)) pipe.qk(sb, kst(1), qop);
+      if (act0) {
+        if (needs_mask(kbeg)) mask_tile<BN>(sa, kbeg, kend, row, off, p.causal, g);
+        softmax_tile<DT, BN, NDB>(sa, pa, oacc, m_run, l_run, c_run, sl2);
+      }
+      block_sync();  // key tile 0's stage is free again
+      if (ntiles > 0) {
+        pipe.issue_k(rk, kbeg + 4 * BN, kst(0));
+        pipe.issue_v(rv, kbeg + 2 * BN, vst(2));
+      }
+      P::template wait_loads<2>();  // key tile 2 and value tile 0
+      block_sync();
+
+      auto finish_d = [&]() __attribute__((always_inline)) {
+        P::template wait_loads<2>();
+        block_sync();
+      };
+      // Tiles t and t+1 full (every row sees every key, every wavefront active): no
+      // branch except the rare re-reference.  The next tile's probabilities are packed
+      // speculatively and packed again if the reference moves.
+      auto step_full = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
+                           f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB], const PTile<DT, BN>& pcur,
+                           PTile<DT, BN>& pnext) __attribute__((always_inline)) {
+        const int k0 = kbeg + t * BN;
+        pipe.issue_k(rk, k0 + 5 * BN, kdst);
+        pipe.issue_v(rv, k0 + 3 * BN, vdst);
+        KOps<DT, D, BN> ko;
+        VOps<DT, D, BN> vo;
+        load_kops<DT, D, BN>(ko, kb, pipe.ln);
+        load_vops<DT, D, BN>(vo, vb, pipe.ln);
+        qk_regs<DT, D, BN>(s_next, ko, qop);
+        pv_regs<DT, D, BN>(oacc, pcur, vo);
+        f32x16_t pr[NKB];
+        float ls = softmax_exp_ref<BN>(s_cur, pr, m_run, sl2);
+        float cs = pack_bf16<BN>(pr, pnext);
+        interleave_deferred<D, BN>();
+        // (cs is in the test only so that the packing stays ahead of the branch; it is
+        // close to ls and non-finite exactly when ls is)
+        if (__builtin_amdgcn_ballot_w64(!(ls + cs <= 2.0f * kSumCap))) {
+          ls = softmax_redo<BN, NDB>(s_cur, pr, oacc, m_run, l_run, c_run, sl2);
+          cs = pack_bf16<BN>(pr, pnext);
+        }
+        l_run += ls;
+        c_run += cs;
+        finish_d();
+      };
+      // Everything else: the causal diagonal band, the sequence / chunk tail, the last
+      // tiles, and the cadence-keeping iterations past the range.
+      auto step_edge = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
+                           f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB], const PTile<DT, BN>& pcur,
+                           PTile<DT, BN>& pnext) __attribute__((always_inline)) {
+        const int k0 = kbeg + t * BN;
+        const bool act_t = t < ntiles && active(k0);
+        const bool act_1 = t + 1 < ntiles && active(k0 + BN);
+        const bool act_2 = t + 2 < ntiles && active(k0 + 2 * BN);
+        pipe.issue_k(rk, k0 + 5 * BN, kdst);
+        pipe.issue_v(rv, k0 + 3 * BN, vdst);
+        if (act_2) pipe.qk(s_next, kb, qop);
+        if (act_t) pipe.pv(oacc, s_cur, pcur, vb);
+        if (act_1) {
+          if (needs_mask(k0 + BN)) mask_tile<BN>(s_cur, k0 + BN, kend, row, off, p.causal, g);
+          softmax_tile<DT, BN, NDB>(s_cur, pnext, oacc, m_run, l_run, c_run, sl2);
+        }
+        finish_d();
+      };
+      // Leading tiles that are full: inside [kbeg, kend), (causal) below the diagonal
+      // of the tile's first row, and every wavefront has rows.  Iteration t of the
+      // full loop needs tiles t and t+1 full; the count is rounded down to a multiple
+      // of U so that both loops start on stage 0 with constant stage indices.
+      int nfull = (kend - kbeg) / BN;
+      if (p.causal) {
+        const int d = q0 + off - kbeg - (BN - 1);
+        nfull = min(nfull, d < 0 ? 0 : d / BN + 1);
+      }
+      if (r0 >= p.Sq) nfull = 0;
+      nfull = nfull - 1 < 0 ? 0 : ((nfull - 1) / U) * U;
+      auto run = [&](auto full_c, int t0, int t1) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_c)::value;
+        for (int t = t0; t < t1; t += U) {
+#pragma unroll
+          for (int j = 0; j < U; ++j) {
+            if (FULL || t + j < t1) {
+              uint8_t* kd = kst(j + 1);
+              uint8_t* vd = vst(j + 3);
+              const uint8_t* kb = kst(j + 2);
+              const uint8_t* vb = vst(j);
+              if (j % 2 == 0) {
+                if constexpr (FULL) step_full(t + j, kd, vd, kb, vb, sb, sa, pa, pb);
+                else step_edge(t + j, kd, vd, kb, vb, sb, sa, pa, pb);
+              } else {
+                if constexpr (FULL) step_full(t + j, kd, vd, kb, vb, sa, sb, pb, pa);
+                else step_edge(t + j, kd, vd, kb, vb, sa, sb, pb, pa);
+              }
+            }
+          }
+        }
+      };
+      run(std::true_type{}, 0, nfull);
+      run(std::false_type{}, nfull, ntiles);
+      wait_vmem();
+      block_sync();
+    } else {
+
     // prologue: key tiles 0..NS-1 and value tiles 0..NS-2 in flight, then S^T of tile
     // 0 once key tile 0 has landed.  Loads are issued unconditionally (tiles past the
     // end are never used; past the sequence they read as zeros) so that every
@@ -963,29 +1126,9 @@ void attn_fwd_kernel(FwdArgs p) {
       pipe.issue_k(rk, k0 + NS * BN, kdst);
       pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
       PTile<DT, BN> pt;
-      if constexpr (P::kRegOps) {
-        // Both operand sets are read first (their LDS latency overlaps the row
-        // maximum), then the MFMAs of tile t+1 (S^T) and tile t (values) interleave
-        // with the exponentials and sums of tile t.
-        KOps<DT, D, BN> ko;
-        VOps<DT, D, BN> vo;
-        load_kops<DT, D, BN>(ko, kb, pipe.ln);
-        load_vops<DT, D, BN>(vo, vb, pipe.ln);
-        qk_regs<DT, D, BN>(s_next, ko, qop);
-        f32x16_t pr[NKB];
-        float ls = softmax_exp_ref<BN>(s_cur, pr, m_run, sl2);
-        interleave_exp<D, BN>();
-        if (__builtin_amdgcn_ballot_w64(!(ls <= kSumCap)))
-          ls = softmax_redo<BN, NDB>(s_cur, pr, oacc, m_run, l_run, c_run, sl2);
-        l_run += ls;
-        c_run += pack_bf16<BN>(pr, pt);
-        pv_regs<DT, D, BN>(oacc, pt, vo);
-        interleave_pv<D, BN>();
-      } else {
-        pipe.qk(s_next, kb, qop);
-        softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
-        pipe.pv(oacc, s_cur, pt, vb);
-      }
+      pipe.qk(s_next, kb, qop);
+      softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
+      pipe.pv(oacc, s_cur, pt, vb);
       finish(kdst, vdst);
     };
     // Remaining tiles: the causal diagonal band, the sequence / chunk tail, the last
@@ -1050,6 +1193,7 @@ void attn_fwd_kernel(FwdArgs p) {
     // Drain every load before the rings are reused, by this group or the next sweep.
     wait_vmem();
     block_sync();
+    }
   };
 
   // ---- write-back: deferred normalisation
