@@ -772,7 +772,26 @@ __device__ __forceinline__ void sched_pairs() {
   }
 }
 
-// Interleave for the bf16 main loop (no row maximum): each of the iteration's MFMAs
+// Interleave for the bf16 main loop (no row maximum), whose tile step has two
+// scheduling regions (before and after the rare re-reference branch): the S^T MFMAs of
+// the next tile with the exponentials and the exact sum, then the value MFMAs with the
+// conversion and the consistent sum.
+template <int D, int BN>
+__device__ __forceinline__ void interleave_exp() {
+  constexpr int NKB = BN / 32;
+  constexpr int NQ = (D / 16) * NKB;
+  constexpr int VE = NKB * 48;                // fma + exp + add per score
+  sched_pairs<NQ, 0x8, 1, 0x2, (VE + NQ - 1) / NQ>();
+}
+template <int D, int BN>
+__device__ __forceinline__ void interleave_pv() {
+  constexpr int NKB = BN / 32;
+  constexpr int NP = NKB * 2 * (D / 32);
+  constexpr int VS = NKB * 16;                // converts and dot products
+  sched_pairs<NP, 0x8, 1, 0x2, (VS + NP - 1) / NP>();
+}
+
+// Interleave for the deferred bf16 main loop: each of the iteration's MFMAs
 // (S^T of tile t+2, then P(t) V(t)) is followed by a share of the VALU work on tile
 // t+1 -- exponentials, row sum, bf16 packing and the sum of the packed values -- none
 // of which the MFMAs depend on.
@@ -938,6 +957,7 @@ void attn_fwd_kernel(FwdArgs p) {
   // The sweep is unrolled by U tiles: a multiple of NS (constant stages) and of 2 (the
   // two score buffers alternate).
   constexpr int U = NS % 2 == 0 ? NS : 2 * NS;
+  constexpr bool kDeferred = P::kRegOps && MODE != kPairs;
 
   // ---- key sweep over keys [kbeg, kend) of the current query tile, in `ntiles`
   // iterations.  Every group of the workgroup passes the same number of barriers
@@ -953,8 +973,9 @@ void attn_fwd_kernel(FwdArgs p) {
       return (k0 + BN > kend) || (p.causal && (k0 + BN - 1 > r0 + off));
     };
 
-    if constexpr (P::kRegOps) {
-      // ---- deferred pipeline (bf16, d <= 128).  Iteration t computes S^T of key tile
+    if constexpr (kDeferred) {
+      // ---- deferred pipeline (bf16, d <= 128; not the causal pair mode, whose two sweeps
+      // per group pay the longer prologue twice: measured 2-5 % slower there).  Iteration t computes S^T of key tile
       // t+2, adds P(t) V(t) with the probabilities packed in iteration t-1, and turns
       // the scores of tile t+1 into P(t+1): none of the iteration's MFMAs waits for
       // its own exponentials, so the two interleave freely.  Tile j's keys and values
@@ -1126,9 +1147,29 @@ void attn_fwd_kernel(FwdArgs p) {
       pipe.issue_k(rk, k0 + NS * BN, kdst);
       pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
       PTile<DT, BN> pt;
-      pipe.qk(s_next, kb, qop);
-      softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
-      pipe.pv(oacc, s_cur, pt, vb);
+      if constexpr (P::kRegOps) {
+        // Both operand sets are read first (their LDS latency overlaps the row
+        // maximum), then the MFMAs of tile t+1 (S^T) and tile t (values) interleave
+        // with the exponentials and sums of tile t.
+        KOps<DT, D, BN> ko;
+        VOps<DT, D, BN> vo;
+        load_kops<DT, D, BN>(ko, kb, pipe.ln);
+        load_vops<DT, D, BN>(vo, vb, pipe.ln);
+        qk_regs<DT, D, BN>(s_next, ko, qop);
+        f32x16_t pr[NKB];
+        float ls = softmax_exp_ref<BN>(s_cur, pr, m_run, sl2);
+        interleave_exp<D, BN>();
+        if (__builtin_amdgcn_ballot_w64(!(ls <= kSumCap)))
+          ls = softmax_redo<BN, NDB>(s_cur, pr, oacc, m_run, l_run, c_run, sl2);
+        l_run += ls;
+        c_run += pack_bf16<BN>(pr, pt);
+        pv_regs<DT, D, BN>(oacc, pt, vo);
+        interleave_pv<D, BN>();
+      } else {
+        pipe.qk(s_next, kb, qop);
+        softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
+        pipe.pv(oacc, s_cur, pt, vb);
+      }
       finish(kdst, vdst);
     };
     // Remaining tiles: the causal diagonal band, the sequence / chunk tail, the last
