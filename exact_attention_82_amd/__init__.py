@@ -7,10 +7,12 @@ kernels.  There is no fallback: if the library is not built, or a call is refuse
 exception is raised.
 
     o, lse = attn_fwd(q, k, v, scale=None, causal=False)
+    o, lse = attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
     ws = attn_fwd_splitkv(q, k, v, num_splits, ...)
     o, lse = attn_merge(ws, num_splits, B, H, Sq, d)
 
-Tensors are [B, H, S, d] contiguous on the GPU: torch.float32, torch.bfloat16, or FP8
+Tensors are [B, H, S, d] contiguous on the GPU (ragged batches: [H, total, d] with int32
+sequence offsets): torch.float32, torch.bfloat16, or FP8
 E4M3FN codes (torch.float8_e4m3fn, or torch.uint8 holding the codes).  Outputs are
 float32.
 """
@@ -24,7 +26,7 @@ from . import _lib
 from ._lib import ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3, ATTN_MAX_SPLITS, AttnError  # noqa: F401
 
 __all__ = [
-    "attn_fwd", "attn_fwd_splitkv", "attn_merge", "attn_splitkv_workspace_bytes",
+    "attn_fwd", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_merge", "attn_splitkv_workspace_bytes",
     "attn_block_m", "attn_block_n", "attn_num_workgroups", "attn_kernel_name",
     "attn_status_string", "attn_last_hip_error", "dtype_code", "library_path", "AttnError",
 ]
@@ -84,6 +86,40 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None)
                               ctypes_ptr(lse), B, H, Sq, Sk, d, float(scale), int(causal), dt,
                               _stream(stream))
     _lib.check("attn_fwd", st)
+    return out, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    scale=None, causal=False, out=None, lse=None, stream=None):
+    """attn_fwd over B packed sequences: q [H, total_q, d], k and v [H, total_k, d],
+    cu_seqlens_* int32 [B+1] offsets on the GPU; O [H, total_q, d] and lse [H, total_q]
+    (float32).  Sequence b uses rows cu[b]:cu[b+1] of every head and its own keys only."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [H, total, d]")
+    H, total_q, d = q.shape
+    total_k = k.shape[1]
+    if tuple(k.shape) != (H, total_k, d) or tuple(v.shape) != (H, total_k, d):
+        raise ValueError("k and v must be [H, total_k, d] with q's H and d")
+    dt = dtype_code(q)
+    if dtype_code(k) != dt or dtype_code(v) != dt:
+        raise TypeError("q, k and v must share one dtype")
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or c.dim() != 1:
+            raise TypeError("cu_seqlens must be 1-D int32 tensors")
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((H, total_q, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    st = _lib.load().attn_fwd_varlen(
+        ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out), ctypes_ptr(lse),
+        ctypes_ptr(cu_seqlens_q), ctypes_ptr(cu_seqlens_k), B, H, int(max_seqlen_q),
+        int(max_seqlen_k), total_q, total_k, d, float(scale), int(causal), dt, _stream(stream))
+    _lib.check("attn_fwd_varlen", st)
     return out, lse
 
 

@@ -87,6 +87,39 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, float* o, floa
   return launched(attn::launch_fwd(a, stream));
 }
 
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int B, int H, int max_seqlen_q, int max_seqlen_k,
+                            int total_q, int total_k, int d, float scale, int causal,
+                            attn_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+  if (total_q < 1 || total_k < 1) return ATTN_ERR_SHAPE;
+  // the per-sequence limits are those of a dense call with the largest lengths
+  attn_status st = check_shape(B, H, max_seqlen_q, max_seqlen_k, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (int64_t(H) * total_q * d >= kMaxIndex || int64_t(H) * total_k * d >= kMaxIndex)
+    return ATTN_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return ATTN_ERR_ALIGN;
+  if ((causal != 0 && causal != 1) || !positive_finite(scale)) return ATTN_ERR_ARG;
+  const float sl2 = static_cast<float>(double(scale) * kLog2e);
+  if (!positive_finite(sl2)) return ATTN_ERR_ARG;
+
+  attn::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.Sq = max_seqlen_q; a.Sk = max_seqlen_k; a.d = d;
+  a.dtype = dtype; a.causal = causal;
+  a.num_splits = 1; a.chunk = max_seqlen_k; a.split_mode = 0;
+  a.scale_log2 = sl2;
+  a.v_scale = 1.0f;
+  a.pair_order = 0;  // plain kernel: one workgroup per (sequence, head, 128-row tile)
+  a.head_group = 1;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  a.total_q = total_q; a.total_k = total_k;
+  return launched(attn::launch_fwd(a, stream));
+}
+
 size_t attn_splitkv_workspace_bytes(int B, int H, int Sq, int d, int num_splits) {
   if (B < 1 || H < 1 || Sq < 1 || !supported_d(d)) return 0;
   if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return 0;

@@ -40,6 +40,11 @@ struct FwdArgs {
                      // tiles per CU, 2 causal tile pairs shared by the two groups of one
                      // workgroup, 3 two groups splitting each tile's keys (small grids)
   int head_group;    // heads whose query tiles are scheduled together (divides B*H)
+  // Ragged batch (attn_fwd_varlen): sequence offsets per head block, or null.  Then Sq
+  // and Sk hold the largest lengths and q/k/v/o/lse point at [H][total][...] blocks.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
 };
 
 // Launch plan of a forward call: query rows per workgroup and the causal schedule.

@@ -849,7 +849,45 @@ void attn_fwd_kernel(FwdArgs p) {
   const int BH = p.B * p.H;
   const int nqt = ceil_div_i(p.Sq, kBlockM);
   int bh, qt, split = 0;
-  if (MODE == kPairs) {
+  if (MODE == kPlain && p.cu_q != nullptr) {
+    // Ragged batch: workgroup x -> (sequence b, head h, r-th query tile of the
+    // sequence), XCD-contiguous as below; the grid is sized for the longest sequence
+    // and workgroups past their sequence's end leave at once (before any barrier).
+    // The offsets come from device memory: clamped to [0, total] and the lengths to
+    // [0, max_seqlen], so that no entry can move an access outside the buffers.  From
+    // here on the workgroup sees one (batch, head) slice of length Sq x Sk, as in a
+    // dense call with B = H = 1.
+    int x = blockIdx.x;
+    const int nwg = gridDim.x;
+    if ((nwg & 7) == 0) x = (x & 7) * (nwg >> 3) + (x >> 3);
+    const int r = x % nqt;
+    const int sh = x / nqt;
+    const int b = sh / p.H, h = sh % p.H;
+    auto span = [](const int32_t* cu, int b, int total, int maxlen, int& lo) {
+      const long long a = cu[b], e = cu[b + 1];
+      lo = int(a < 0 ? 0 : a > total ? total : a);
+      long long n = e - lo;
+      n = n < 0 ? 0 : n;
+      n = n > maxlen ? maxlen : n;
+      n = n > total - lo ? total - lo : n;
+      return int(n);
+    };
+    int q_lo, k_lo;
+    const int q_len = span(p.cu_q, b, p.total_q, p.Sq, q_lo);
+    const int k_len = span(p.cu_k, b, p.total_k, p.Sk, k_lo);
+    const int nqt_b = ceil_div_i(q_len, kBlockM);
+    if (r >= nqt_b) return;
+    qt = p.causal ? nqt_b - 1 - r : r;  // causal: longest sweeps first
+    bh = 0;
+    const int64_t qrow = int64_t(h) * p.total_q + q_lo, krow = int64_t(h) * p.total_k + k_lo;
+    p.q = reinterpret_cast<const uint8_t*>(p.q) + qrow * D * EB;
+    p.k = reinterpret_cast<const uint8_t*>(p.k) + krow * D * EB;
+    p.v = reinterpret_cast<const uint8_t*>(p.v) + krow * D * EB;
+    p.o += qrow * D;
+    p.lse += qrow;
+    p.Sq = q_len;
+    p.Sk = k_len;
+  } else if (MODE == kPairs) {
     // batch*head fastest: all pairs of a head land on one XCD (index mod 8).
     bh = blockIdx.x % BH;
     qt = blockIdx.x / BH;              // the lighter tile t of the pair

@@ -84,6 +84,41 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, float* o, floa
                      attn_dtype dtype, void* stream);
 
 /*
+ * attn_fwd_varlen -- attn_fwd over a ragged batch: B sequences of different lengths
+ * packed without padding (variable-length sequences handled as ragged tensors, as the
+ * page "Inside FlashAttention-3", section 7.2, lists for the production integration).
+ *
+ * Layout (head-major, packed): Q is [H, total_q, d], K and V are [H, total_k, d], O is
+ * [H, total_q, d] fp32 and lse is [H, total_q] fp32, all contiguous.  Sequence b owns the
+ * query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and the key rows
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]) of every head and attends only to its own keys:
+ * for each sequence the result is that of attn_fwd with B = 1, Sq = its query count and
+ * Sk = its key count (the causal mask aligned to that sequence's bottom-right corner; a
+ * sequence with queries but no keys gets O = 0 and lse = -inf on its rows).
+ *
+ *   cu_seqlens_q, cu_seqlens_k  device pointers to int32 [B+1] (4-byte aligned):
+ *                 non-decreasing offsets from 0 to total_q / total_k, each length at
+ *                 most max_seqlen_q / max_seqlen_k.  The kernel reads them; the host
+ *                 cannot check them without synchronising, which the library never
+ *                 does.  Offsets are clamped to [0, total] and lengths to
+ *                 [0, max_seqlen] on the device, so entries that break the contract can
+ *                 never make a kernel address outside the buffers; they give
+ *                 unspecified results.  Rows that no sequence covers are not written.
+ *   max_seqlen_q, max_seqlen_k  bounds of the lengths, >= 1; the launch has
+ *                 B * H * ceil(max_seqlen_q / 128) four-wavefront workgroups, and those
+ *                 past the end of their sequence exit at once.
+ *   total_q, total_k  rows per head of Q (and O) and of K / V, >= 1
+ * Everything else as for attn_fwd (all dtypes and head dims; fp8 codes used as they
+ * are).  The launch is the plain kernel instance of attn_fwd for (d, dtype), the one
+ * attn_kernel_name reports for a non-causal call.
+ */
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int B, int H, int max_seqlen_q, int max_seqlen_k,
+                            int total_q, int total_k, int d, float scale, int causal,
+                            attn_dtype dtype, void* stream);
+
+/*
  * attn_splitkv_workspace_bytes -- bytes of the workspace attn_fwd_splitkv writes and
  * attn_merge reads for this shape, or 0 if an argument is out of range.
  *

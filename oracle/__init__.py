@@ -11,6 +11,6 @@ the pages, closed forms, invariants and a 50-digit brute force on tiny inputs.
 """
 from .attention import (  # noqa: F401
     visible_mask, scores, softmax_probs, attention, split_bounds, partial_state,
-    split_states, merge_states, naive_average, attention_split, flops,
+    split_states, merge_states, naive_average, attention_split, attention_varlen, flops,
 )
 from .backward import attention_bwd, row_dot  # noqa: F401

@@ -32,6 +32,7 @@ import numpy as np
 __all__ = [
     "visible_mask", "scores", "softmax_probs", "attention", "split_bounds",
     "partial_state", "split_states", "merge_states", "naive_average", "attention_split",
+    "attention_varlen",
 ]
 
 
@@ -177,6 +178,32 @@ def naive_average(states):
 def attention_split(q, k, v, scale, n, causal=False, Sq_total=None, q_index=None):
     """Attention through an n-way key split and merge: (O, lse)."""
     return merge_states(split_states(q, k, v, scale, n, causal, Sq_total, q_index))
+
+
+# ----------------------------------------------------------------------------- ragged batch
+def attention_varlen(q, k, v, cu_q, cu_k, scale, causal=False):
+    """Exact attention of a ragged batch: (O [H, total_q, d], lse [H, total_q]).
+
+    Variable-length sequences packed as ragged tensors ("Inside FlashAttention-3" page,
+    section 7.2): q is [H, total_q, d], k and v are [H, total_k, d]; sequence b owns
+    query rows cu_q[b]:cu_q[b+1] and key rows cu_k[b]:cu_k[b+1] of every head and
+    attends to its own keys only, with the causal mask aligned to its own bottom-right
+    corner.  Each sequence is the plain definition above applied to its slices; a
+    sequence with no keys gets O = 0, lse = -inf.  Rows that no sequence covers are NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    H, Tq, d = q.shape
+    o = np.full((H, Tq, d), np.nan)
+    lse = np.full((H, Tq), np.nan)
+    for b in range(len(cu_q) - 1):
+        a, e = int(cu_q[b]), int(cu_q[b + 1])
+        ka, ke = int(cu_k[b]), int(cu_k[b + 1])
+        if e <= a:
+            continue
+        o[:, a:e], lse[:, a:e] = attention(q[:, a:e], k[:, ka:ke], v[:, ka:ke], scale, causal)
+    return o, lse
 
 
 def flops(B: int, H: int, Sq: int, Sk: int, d: int, causal: bool) -> float:

@@ -181,6 +181,26 @@ def make_attention_inputs(B: int, H: int, Sq: int, Sk: int, d: int, seed: int,
                            (sq, sk, sv), hot)
 
 
+def varlen_lengths(n: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """``n`` sequence lengths drawn uniformly from [lo, hi] (int64), seeded."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi + 1, size=n).astype(np.int64)
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    """Offsets [0, l0, l0+l1, ...] (int32) of sequences packed one after another."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def make_varlen_inputs(lens_q, lens_k, H: int, d: int, seed: int, dtype: str = "bf16"):
+    """A ragged batch packed head-major: Q [H, sum(lens_q), d], K and V [H, sum(lens_k), d],
+    drawn and rounded exactly like ``make_attention_inputs`` with B = 1 (one fp8 scale per
+    packed tensor).  Returns (AttentionInputs with [1, H, total, d] arrays, cu_q, cu_k)."""
+    cu_q, cu_k = cu_seqlens(lens_q), cu_seqlens(lens_k)
+    inp = make_attention_inputs(1, H, max(int(cu_q[-1]), 1), max(int(cu_k[-1]), 1), d, seed, dtype)
+    return inp, cu_q, cu_k
+
+
 def worked_example_inputs(d: int = 64, dtype: str = "bf16") -> AttentionInputs:
     """The page's 1x4 worked example embedded in a d-dimensional head.
 

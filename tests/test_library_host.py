@@ -31,7 +31,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for n in ("attn_fwd", "attn_fwd_splitkv", "attn_merge", "attn_splitkv_workspace_bytes"):
+    for n in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_merge",
+              "attn_splitkv_workspace_bytes"):
         assert n in names
 
 
@@ -61,6 +62,27 @@ def fwd(lib, *, q=Q, k=K, v=V, o=O, l=L, B=1, H=1, Sq=8, Sk=8, d=64, scale=0.125
 ])
 def test_attn_fwd_refuses_bad_arguments(lib, kw, status):
     assert fwd(lib, **kw) == status
+
+
+CQ, CK = 0x70000, 0x70100  # fake int32 offset arrays
+
+
+def varlen(lib, *, q=Q, k=K, v=V, o=O, l=L, cq=CQ, ck=CK, B=2, H=1, mq=8, mk=8, tq=16, tk=16,
+           d=64, scale=0.125, causal=0, dtype=1):
+    return lib.attn_fwd_varlen(q, k, v, o, l, cq, ck, B, H, mq, mk, tq, tk, d, scale, causal, dtype,
+                               None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(cq=None), 1), (dict(ck=None), 1),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(mq=0), 2), (dict(mk=0), 2), (dict(tq=0), 2),
+    (dict(tk=-3), 2), (dict(H=1 << 20, tq=1 << 20, d=128), 2), (dict(mq=1 << 30), 2),
+    (dict(d=96), 4), (dict(dtype=5), 4),
+    (dict(q=Q + 8), 3), (dict(cq=CQ + 2), 3), (dict(ck=CK + 1), 3),
+    (dict(causal=3), 7), (dict(scale=0.0), 7), (dict(scale=math.nan), 7),
+])
+def test_attn_fwd_varlen_refuses_bad_arguments(lib, kw, status):
+    assert varlen(lib, **kw) == status
 
 
 def test_splitkv_and_merge_refuse_bad_arguments(lib):
