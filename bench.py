@@ -274,6 +274,48 @@ def sweep(name: str, reps: int, warmup: int):
             del q, k, v, o, lse
             torch.cuda.empty_cache()
         return
+    if name == "varlen":
+        # ragged batches: 16 sequences of 256..4096 tokens (uniform, seeded), H=16, bf16;
+        # useful FLOPs = sum over sequences of 4*H*l^2*d (half causal).  The same batch
+        # padded to its longest sequence and run through attn_fwd is timed beside it.
+        for d, seed in ((64, 31), (128, 32)):
+            H = 16
+            lens = si.varlen_lengths(16, 256, 4096, seed=seed)
+            inp, cu_q, cu_k = si.make_varlen_inputs(lens, lens, H, d, seed=seed + 100, dtype="bf16")
+            q, k, v = (t[0] for t in to_dev(inp))
+            del inp
+            cq, ck = torch.from_numpy(cu_q).to(dev), torch.from_numpy(cu_k).to(dev)
+            T, M, B = int(cu_q[-1]), int(lens.max()), len(lens)
+            o = torch.empty((H, T, d), dtype=torch.float32, device=dev)
+            lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+            pad = si.make_attention_inputs(B, H, M, M, d, seed=seed + 200, dtype="bf16")
+            pq, pk, pv = to_dev(pad)
+            del pad
+            po = torch.empty((B, H, M, d), dtype=torch.float32, device=dev)
+            pl = torch.empty((B, H, M), dtype=torch.float32, device=dev)
+            scale = float(np.float32(1.0 / np.sqrt(d)))
+            for causal in (False, True):
+                fn = lambda: ea.attn_fwd_varlen(q, k, v, cq, ck, M, M, scale=scale, causal=causal,
+                                                out=o, lse=lse)
+                fp = lambda: ea.attn_fwd(pq, pk, pv, scale=scale, causal=causal, out=po, lse=pl)
+                for _ in range(warmup):
+                    fn()
+                    fp()
+                torch.cuda.synchronize()
+                us = _timed_calls(fn, reps, flush)
+                pus = _timed_calls(fp, reps, flush)
+                fl = float(sum(4.0 * H * int(l) * int(l) * d for l in lens)) / (2.0 if causal else 1.0)
+                tf = fl / (float(np.median(us)) * 1e-6) / 1e12
+                emit({"workload": "varlen", "B": B, "H": H, "d": d, "dtype": "bf16", "causal": causal,
+                      "lengths": [int(l) for l in lens], "total": T, "max_len": M,
+                      "kernel": ea.attn_kernel_name(1, H, M, d, 0, ea.ATTN_BF16), "reps": reps,
+                      **_stats(us), "tflops": round(tf, 2),
+                      "pct_of_bound": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+                      "padded_dense": {**_stats(pus),
+                                       "tflops_useful": round(fl / (float(np.median(pus)) * 1e-6) / 1e12, 2)}})
+            del q, k, v, o, lse, pq, pk, pv, po, pl
+            torch.cuda.empty_cache()
+        return
     if name == "bwd":
         import oracle
         for (B, H, S, d, seed) in ((1, 8, 8192, 128, 3), (8, 32, 2048, 64, 2), (1, 16, 2048, 256, 421)):
@@ -358,6 +400,16 @@ def summarize_sweep(path: str) -> str:
     """Markdown table of the JSON lines written by --sweep."""
     recs = [json.loads(l) for l in open(path) if l.strip().startswith("{")]
     out = []
+    if recs and recs[0]["workload"] == "varlen":
+        out += ["| sequences | H | d | tokens | longest | mask | kernel | median us | TFLOP/s | % of 2500 | padded dense median us | padded dense TFLOP/s (useful) |",
+                "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+        for r in recs:
+            pd = r["padded_dense"]
+            out.append(f"| {r['B']} | {r['H']} | {r['d']} | {r['total']} | {r['max_len']} | "
+                       f"{'causal' if r['causal'] else 'full'} | {r['kernel']} | {r['median_us']} | "
+                       f"{r['tflops']} | {r['pct_of_bound']} | {pd['median_us']} | {pd['tflops_useful']} |")
+        out.append("\nlengths: " + "; ".join(f"d={r['d']}: {r['lengths']}" for r in recs if not r["causal"]))
+        return "\n".join(out)
     if recs and recs[0]["workload"] == "c5":
         out += ["| n | kernel | splitkv median us | merge median us | total us | GB/s (alg.) | GB/s (with ws) | % of 8 TB/s |",
                 "|---|---|---|---|---|---|---|---|"]
@@ -391,7 +443,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
-    ap.add_argument("--sweep", choices=("c1", "c2", "c4", "c5", "bwd"),
+    ap.add_argument("--sweep", choices=("c1", "c2", "c4", "c5", "bwd", "varlen"),
                     help="per-case timing of a parity workload (JSON lines)")
     ap.add_argument("--sweep-reps", type=int, default=30)
     ap.add_argument("--summarize-sweep", metavar="JSONL")

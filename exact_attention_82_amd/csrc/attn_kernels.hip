@@ -850,18 +850,26 @@ void attn_fwd_kernel(FwdArgs p) {
   const int nqt = ceil_div_i(p.Sq, kBlockM);
   int bh, qt, split = 0;
   if (MODE == kPlain && p.cu_q != nullptr) {
-    // Ragged batch: workgroup x -> (sequence b, head h, r-th query tile of the
-    // sequence), XCD-contiguous as below; the grid is sized for the longest sequence
-    // and workgroups past their sequence's end leave at once (before any barrier).
-    // The offsets come from device memory: clamped to [0, total] and the lengths to
-    // [0, max_seqlen], so that no entry can move an access outside the buffers.  From
-    // here on the workgroup sees one (batch, head) slice of length Sq x Sk, as in a
-    // dense call with B = H = 1.
-    int x = blockIdx.x;
-    const int nwg = gridDim.x;
-    if ((nwg & 7) == 0) x = (x & 7) * (nwg >> 3) + (x >> 3);
-    const int r = x % nqt;
-    const int sh = x / nqt;
+    // Ragged batch: workgroup -> (sequence b, head h, r-th query tile of the sequence);
+    // the grid is sized for the longest sequence and workgroups past their sequence's
+    // end leave at once (before any barrier).  Slice s = b*H + h runs on XCD s % 8 (the
+    // dispatcher sends workgroup i to XCD i % 8), all its tiles in a row: the XCDs get
+    // the heads of every sequence in equal shares whatever the lengths, and each slice's
+    // keys stream through one L2.  (A contiguous range of sequences per XCD, as for
+    // dense calls, leaves the XCDs with the short sequences idle.)  The offsets come from
+    // device memory: clamped to [0, total] and the lengths to [0, max_seqlen], so that no
+    // entry can move an access outside the buffers.  From here on the workgroup sees one
+    // (batch, head) slice of length Sq x Sk, as in a dense call with B = H = 1.
+    const int nslices = p.B * p.H;
+    int r, sh;
+    if ((nslices & 7) == 0) {
+      const int j = blockIdx.x & 7, i = blockIdx.x >> 3;
+      sh = j + 8 * (i / nqt);
+      r = i % nqt;
+    } else {
+      sh = blockIdx.x / nqt;
+      r = blockIdx.x % nqt;
+    }
     const int b = sh / p.H, h = sh % p.H;
     auto span = [](const int32_t* cu, int b, int total, int maxlen, int& lo) {
       const long long a = cu[b], e = cu[b + 1];
