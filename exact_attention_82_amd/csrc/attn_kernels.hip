@@ -48,6 +48,7 @@ typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -67,13 +68,16 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // ------------------------------------------------------------------ element traits
-// kKPL: contraction elements one lane supplies per MFMA; kKS: contraction depth of one
-// MFMA (two lane halves); kTau: lazy-rescale threshold in log2 units; kDMA: tiles
-// reach LDS by direct buffer-to-LDS loads (else through registers).
+// Op: one lane's operand of the S^T MFMA (and of the value MFMA); POp: the packed
+// probabilities of one 16-key step; kKPL: contraction elements one lane supplies per
+// MFMA; kKS: contraction depth of one MFMA (two lane halves); kTau: lazy-rescale
+// threshold in log2 units; kDMA: tiles reach LDS by direct buffer-to-LDS loads (else
+// through registers).
 template <int DT> struct Traits;
 
 template <> struct Traits<DT_BF16> {
   using Op = bf16x8_t;
+  using POp = bf16x8_t;
   static constexpr int kBytes = 2, kKPL = 8, kKS = 16;
   static constexpr bool kDMA = true;
   static constexpr float kTau = 8.0f;
@@ -83,21 +87,27 @@ template <> struct Traits<DT_BF16> {
   }
 };
 
+// FP8 uses gfx950's 32x32x64 MFMA (32 bytes per lane, unit E8M0 block scales = 127):
+// the 32x32x16 FP8 MFMA inherited from gfx942 runs at the bf16 rate on this chip, the
+// 32x32x64 one at twice that (measured 2.0 vs 4.3 PFLOP/s).
 template <> struct Traits<DT_FP8> {
-  using Op = long;
-  static constexpr int kBytes = 1, kKPL = 8, kKS = 16;
+  using Op = i32x8_t;
+  using POp = long;
+  static constexpr int kBytes = 1, kKPL = 32, kKS = 64;
   static constexpr bool kDMA = true;
   // FP8 probabilities are scaled by 2^8 before rounding to E4M3 (max 448) so that
   // they sit in the format's normal range; the exact rescale keeps them <= 1 first.
   static constexpr float kTau = 0.0f;
   static constexpr float kPScale = 256.0f;
   __device__ static f32x16_t mfma(Op a, Op b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, c, 0, 0, 0);
+    // formats 0 / 0: E4M3 for both operands; scales 127 = 2^0
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
   }
 };
 
 template <> struct Traits<DT_F32> {
   using Op = float;
+  using POp = float;
   static constexpr int kBytes = 4, kKPL = 1, kKS = 2;
   static constexpr bool kDMA = false;
   static constexpr float kTau = 8.0f;
@@ -213,11 +223,13 @@ __device__ __forceinline__ void dma_tile_at(const Slice& sl, uint8_t* stage, int
 template <int DT, int D, int BN> struct DmaLane {
   using G = DmaGeo<DT, D, BN>;
   int kx;      // key operand: row c, this lane's half g, swizzle folded in
+  int kx2;     // fp8: the second 16-byte chunk of the lane's 32-byte key operand
   int vx[2];   // value operand (bf16: two transposed reads; fp8: one)
   __device__ __forceinline__ DmaLane(int lane) {
     const int c = lane & 31, g = lane >> 5;
     if constexpr (DT == DT_BF16) {
       kx = c * G::ROWB + ((g ^ swz_k<G::ROWB>(c)) << 4);
+      kx2 = 0;
       const int q = (lane & 15) >> 2, hi = (lane >> 4) & 1, lo2 = (lane & 3) >> 1;
       const int qhi = G::ROWB >= 256 ? q : (q >> 1);
 #pragma unroll
@@ -225,11 +237,16 @@ template <int DT, int D, int BN> struct DmaLane {
         vx[B] = (g * 4 + 8 * B + q) * G::ROWB + (qhi << 6) +
                 ((((hi << 1) | lo2) ^ ((g + 2 * B) & 3)) << 4) + ((lane & 1) << 3);
     } else {
-      kx = c * G::ROWB + (swz_k<G::ROWB>(c) << 4) + g * 8;
+      // 32-byte operands: head-dim bytes 64*ks + 32*g + [0, 32) of key row c, i.e.
+      // chunks 4*ks + 2*g and 4*ks + 2*g + 1, each XOR the row's swizzle (the ks term
+      // is XORed in by the reader: it stays inside the chunk field, 64*ks < ROWB)
+      const int f = swz_k<G::ROWB>(c);
+      kx = c * G::ROWB + (((2 * g) ^ f) << 4);
+      kx2 = c * G::ROWB + (((2 * g + 1) ^ f) << 4);
       const int s = (lane & 15) >> 1, hi = (lane >> 4) & 1;
       const int keyin = s < 4 ? g * 4 + s : 8 + g * 4 + (s - 4);
-      const int f = swz_k<G::ROWB>(keyin);
-      vx[0] = keyin * G::ROWB + ((hi ^ f) << 4) + ((lane & 1) << 3);
+      const int fv = swz_k<G::ROWB>(keyin);
+      vx[0] = keyin * G::ROWB + ((hi ^ fv) << 4) + ((lane & 1) << 3);
       vx[1] = 0;
     }
   }
@@ -238,21 +255,30 @@ template <int DT, int D, int BN> struct DmaLane {
 // S^T = K Q^T for every 32-key block of a tile held in LDS stage kt.
 template <int DT, int D, int BN>
 __device__ __forceinline__ void qk_dma(f32x16_t (&s)[BN / 32], const uint8_t* kt,
-                                       const typename Traits<DT>::Op (&qop)[D / 16],
+                                       const typename Traits<DT>::Op (&qop)[D / Traits<DT>::kKS],
                                        const DmaLane<DT, D, BN>& ln) {
   using TR = Traits<DT>;
   using G = DmaGeo<DT, D, BN>;
   using Op = typename TR::Op;
-  constexpr int KSTEPS = D / 16;
+  constexpr int KSTEPS = D / TR::kKS;
 #pragma unroll
   for (int b = 0; b < BN / 32; ++b) s[b] = f32x16_t{};
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    // bf16: logical chunk 2ks+g; fp8: chunk ks, half g -- XOR on the chunk field
-    const int x = ln.kx ^ (DT == DT_BF16 ? (ks << 5) : (ks << 4));
 #pragma unroll
     for (int b = 0; b < BN / 32; ++b) {
-      const Op a = *reinterpret_cast<const Op*>(kt + x + b * 32 * G::ROWB);
+      Op a;
+      if constexpr (DT == DT_BF16) {
+        // logical chunk 2ks+g -- XOR on the chunk field
+        a = *reinterpret_cast<const Op*>(kt + (ln.kx ^ (ks << 5)) + b * 32 * G::ROWB);
+      } else {
+        // two 16-byte chunks (4ks+2g, 4ks+2g+1): the same head-dim bytes the Q operand
+        // of this lane half holds, in the same order
+        const uint8_t* base = kt + b * 32 * G::ROWB;
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(base + (ln.kx ^ (ks << 6)));
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(base + (ln.kx2 ^ (ks << 6)));
+        a = __builtin_bit_cast(Op, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
       s[b] = TR::mfma(a, qop[ks], s[b]);
     }
   }
@@ -269,11 +295,33 @@ __device__ __forceinline__ void pv_dma(f32x16_t (&oacc)[D / 32], const PTile<DT,
   using G = DmaGeo<DT, D, BN>;
   using Op = typename TR::Op;
   constexpr int NDB = D / 32;
+  if constexpr (DT == DT_FP8) {
+    // One 32x32x64 MFMA per output block: the lane's 32 contraction bytes are the four
+    // 16-key steps (b, h) of the tile in the order (0,0) (0,1) (1,0) (1,1), 8 keys each,
+    // for the value operand (four transposed reads) and the probabilities alike -- the
+    // same pairing of keys as four 32x32x16 MFMAs, so the same sum.
+    static_assert(BN == 64, "fp8 tiles are 64 keys: one 64-deep MFMA per output block");
+    const i32x8_t pb = __builtin_bit_cast(i32x8_t, (long __attribute__((ext_vector_type(4)))){
+        pt.pk[0][0], pt.pk[0][1], pt.pk[1][0], pt.pk[1][1]});
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      i32x2_t r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int roff = ((i >> 1) * 32 + (i & 1) * 16) * G::ROWB;
+        r[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t*)(vt + roff + (ln.vx[0] ^ (db << 5))));
+      }
+      const i32x8_t a = {r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+      oacc[db] = TR::mfma(a, pb, oacc[db]);
+    }
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < BN / 32; ++b) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const Op pb = pt.pk[b][h];
+      const Op pb = pt.pk[b][h];  // bf16: Op == POp
       const int roff = (b * 32 + h * 16) * G::ROWB;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -287,10 +335,6 @@ __device__ __forceinline__ void pv_dma(f32x16_t (&oacc)[D / 32], const PTile<DT,
           typedef short i16x8_t __attribute__((ext_vector_type(8)));
           const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           a = __builtin_bit_cast(Op, both);
-        } else {
-          const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) i32x2_t*)(vt + roff + (ln.vx[0] ^ (db << 5))));
-          a = __builtin_bit_cast(Op, v);
         }
         oacc[db] = TR::mfma(a, pb, oacc[db]);
       }
@@ -474,7 +518,7 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&s)[BN / 32], int k0, int ke
 // packed B operands of each 16-key step (pk[b][h] holds elements 8h..8h+7 of score
 // block b); for fp32 the scores themselves, overwritten in place.
 template <int DT, int BN> struct PTile {
-  typename Traits<DT>::Op pk[BN / 32][2];
+  typename Traits<DT>::POp pk[BN / 32][2];
 };
 template <int BN> struct PTile<DT_F32, BN> {};
 
@@ -685,7 +729,7 @@ template <int DT, int D, int BN, int NW> struct Pipe<DT, D, BN, NW, true> {
   using Op = typename Traits<DT>::Op;
   static constexpr int STAGE_K = G::TILE, STAGE_V = G::TILE;
   static constexpr int NSTAGE = 4;
-  static constexpr int KSTEPS = D / 16;
+  static constexpr int KSTEPS = D / Traits<DT>::kKS;
   // Operands go LDS -> registers ahead of their MFMAs where the registers allow it.
   static constexpr bool kRegOps = DT == DT_BF16 && D <= 128;
   // Wait until at most N iterations' worth of tile loads are still in flight.
@@ -962,7 +1006,9 @@ void attn_fwd_kernel(FwdArgs p) {
       if constexpr (DT == DT_BF16) {
         qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b128(rq, boff, 0, 0));
       } else if constexpr (DT == DT_FP8) {
-        qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b64(rq, boff, 0, 0));
+        const u32x4_t lo = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, boff, 0, 0));
+        const u32x4_t hi = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, boff + 16, 0, 0));
+        qop[ks] = __builtin_bit_cast(Op, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       } else {
         qop[ks] = __builtin_bit_cast(Op, __builtin_amdgcn_raw_buffer_load_b32(rq, boff, 0, 0));
       }
