@@ -373,7 +373,7 @@ def sweep(name: str, reps: int, warmup: int):
         ab = _alg_bytes(B, H, Sq, Sk, d, 1)
         o = torch.empty((B, H, Sq, d), dtype=torch.float32, device=dev)
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
-        for n in (1, 4, 16):
+        for n in (1, 4, 16, 32, 64):
             ws = torch.empty(ea.attn_splitkv_workspace_bytes(B, H, Sq, d, n), dtype=torch.uint8, device=dev)
             f1 = lambda: ea.attn_fwd_splitkv(q, k, v, n, scale=scale, descales=inp.scales, ws=ws)
             f2 = lambda: ea.attn_merge(ws, n, B, H, Sq, d, out=o, lse=lse)

@@ -1475,60 +1475,70 @@ void attn_fwd_kernel(FwdArgs p) {
 // ------------------------------------------------------------------ merge kernel
 // One workgroup of 256 threads per row.  Thread t owns the 16-byte column chunk t % CH
 // (CH = D/4 chunks per row) for the splits s = t / CH, t / CH + NG, ... (NG = 256 / CH
-// split groups), so the n chunk states are read with n / NG independent loads per
-// thread; the group partial sums are then added in LDS in a fixed order (the result
-// does not depend on timing).
+// split groups).  Each thread merges its splits in one pass with a running maximum --
+// the merge of the split-K section of "AI 大模型之 FlashAttention_02" applied one chunk
+// at a time (rescale what is accumulated by exp(m_old - m_new) when the maximum moves) --
+// so all of a row's state loads are independent and in flight together; the NG group
+// states are then combined in LDS in a fixed order (the result does not depend on
+// timing).
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void attn_merge_kernel(MergeArgs a) {
   constexpr int CH = D / 4;
   constexpr int NG = 256 / CH;
   __shared__ f32x4_t part_u[NG][CH];
+  __shared__ float part_m[NG];
   __shared__ float part_l[NG];
-  __shared__ float red[4];
   const int tid = threadIdx.x;
   const int ch = tid % CH, grp = tid / CH;
   const int n = a.num_splits;
   // grid-stride over rows (the grid is capped); the loop bound is uniform per workgroup
   for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-    // global maximum of the chunk maxima (natural-log units; -inf for empty chunks)
-    float M = -__builtin_inff();
-    for (int s = tid; s < n; s += 256) M = __builtin_fmaxf(M, a.ws_m[int64_t(s) * a.rows + row]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, o, 64));
-    if ((tid & 63) == 0) red[tid >> 6] = M;
-    __syncthreads();
-    M = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
-
-    float L = 0.0f;
-    f32x4_t U = {0.f, 0.f, 0.f, 0.f};
-    if (M != -__builtin_inff()) {
-      for (int s = grp; s < n; s += NG) {
-        const int64_t i = int64_t(s) * a.rows + row;
-        const float m = a.ws_m[i];
-        if (m == -__builtin_inff()) continue;
-        const float w = expf(m - M);
-        L += w * a.ws_l[i];
-        U += w * *reinterpret_cast<const f32x4_t*>(a.ws_u + i * D + ch * 4);
+    float Mt = -__builtin_inff(), Lt = 0.0f;  // natural-log units, as stored
+    f32x4_t Ut = {0.f, 0.f, 0.f, 0.f};
+    for (int s = grp; s < n; s += NG) {
+      const int64_t i = int64_t(s) * a.rows + row;
+      const float m = a.ws_m[i];
+      const float l = a.ws_l[i];
+      const f32x4_t u = *reinterpret_cast<const f32x4_t*>(a.ws_u + i * D + ch * 4);
+      if (m == -__builtin_inff()) continue;  // empty chunk: neutral
+      if (m > Mt) {
+        const float c = Mt == -__builtin_inff() ? 0.0f : expf(Mt - m);
+        Lt *= c;
+        Ut *= c;
+        Mt = m;
       }
+      const float w = expf(m - Mt);
+      Lt += w * l;
+      Ut += w * u;
     }
-    part_u[grp][ch] = U;
-    if (ch == 0) part_l[grp] = L;
+    part_u[grp][ch] = Ut;
+    if (ch == 0) {
+      part_m[grp] = Mt;
+      part_l[grp] = Lt;
+    }
     __syncthreads();
     if (grp == 0) {
-      U = part_u[0][ch];
-      L = part_l[0];
+      float M = part_m[0];
 #pragma unroll
-      for (int gi = 1; gi < NG; ++gi) {
-        U += part_u[gi][ch];
-        L += part_l[gi];
+      for (int gi = 1; gi < NG; ++gi) M = __builtin_fmaxf(M, part_m[gi]);
+      float L = 0.0f;
+      f32x4_t U = {0.f, 0.f, 0.f, 0.f};
+      if (M != -__builtin_inff()) {
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          const float mg = part_m[gi];
+          const float w = mg == -__builtin_inff() ? 0.0f : expf(mg - M);
+          L += w * part_l[gi];
+          U += w * part_u[gi][ch];
+        }
       }
       const bool empty = !(L > 0.0f);
       const float inv = empty ? 0.0f : 1.0f / L;
       *reinterpret_cast<f32x4_t*>(a.o + row * D + ch * 4) = U * inv;
       if (ch == 0) a.lse[row] = empty ? -__builtin_inff() : M + logf(L);
     }
-    __syncthreads();  // part_u / part_l / red are reused by the next row
+    __syncthreads();  // part_* are reused by the next row
   }
 }
 
