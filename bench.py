@@ -373,6 +373,7 @@ def sweep(name: str, reps: int, warmup: int):
         ab = _alg_bytes(B, H, Sq, Sk, d, 1)
         o = torch.empty((B, H, Sq, d), dtype=torch.float32, device=dev)
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+        auto_n = ea.attn_splitkv_num_splits(B, H, Sq, Sk, d, ea.ATTN_FP8_E4M3)
         for n in (1, 4, 16, 32, 64):
             ws = torch.empty(ea.attn_splitkv_workspace_bytes(B, H, Sq, d, n), dtype=torch.uint8, device=dev)
             f1 = lambda: ea.attn_fwd_splitkv(q, k, v, n, scale=scale, descales=inp.scales, ws=ws)
@@ -386,7 +387,7 @@ def sweep(name: str, reps: int, warmup: int):
             wsb = n * B * H * Sq * (d + 2) * 4
             t = float(np.median(u1)) + float(np.median(u2))
             emit({"workload": "c5", "B": B, "H": H, "Sq": Sq, "Sk": Sk, "d": d, "dtype": "fp8",
-                  "num_splits": n, "kernel": ea.attn_kernel_name(B, H, Sq, d, 0, ea.ATTN_FP8_E4M3, n),
+                  "num_splits": n, "picked_by_attn_splitkv_num_splits": n == auto_n, "kernel": ea.attn_kernel_name(B, H, Sq, d, 0, ea.ATTN_FP8_E4M3, n),
                   "reps": reps, "splitkv": _stats(u1), "merge": _stats(u2),
                   "total_us": round(t, 2), "alg_bytes": ab, "workspace_bytes_rw": 2 * wsb,
                   "alg_gbs": round(ab / (t * 1e-6) / 1e9, 1),
@@ -414,7 +415,8 @@ def summarize_sweep(path: str) -> str:
         out += ["| n | kernel | splitkv median us | merge median us | total us | GB/s (alg.) | GB/s (with ws) | % of 8 TB/s |",
                 "|---|---|---|---|---|---|---|---|"]
         for r in recs:
-            out.append(f"| {r['num_splits']} | {r['kernel']} | {r['splitkv']['median_us']} | "
+            pick = " (attn_splitkv_num_splits)" if r.get("picked_by_attn_splitkv_num_splits") else ""
+            out.append(f"| {r['num_splits']}{pick} | {r['kernel']} | {r['splitkv']['median_us']} | "
                        f"{r['merge']['median_us']} | {r['total_us']} | {r['alg_gbs']} | "
                        f"{r['with_ws_gbs']} | {r['pct_of_hbm']} |")
         return "\n".join(out)

@@ -27,6 +27,7 @@ from ._lib import ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3, ATTN_MAX_SPLITS, AttnError
 
 __all__ = [
     "attn_fwd", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_merge", "attn_splitkv_workspace_bytes",
+    "attn_splitkv_num_splits",
     "attn_block_m", "attn_block_n", "attn_num_workgroups", "attn_kernel_name",
     "attn_status_string", "attn_last_hip_error", "dtype_code", "library_path", "AttnError",
 ]
@@ -121,6 +122,11 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
         int(max_seqlen_k), total_q, total_k, d, float(scale), int(causal), dt, _stream(stream))
     _lib.check("attn_fwd_varlen", st)
     return out, lse
+
+
+def attn_splitkv_num_splits(B, H, Sq, Sk, d, dtype) -> int:
+    """Split count for attn_fwd_splitkv chosen from the shape (1: do not split)."""
+    return int(_lib.load().attn_splitkv_num_splits(B, H, Sq, Sk, d, int(dtype)))
 
 
 def attn_splitkv_workspace_bytes(B, H, Sq, d, num_splits) -> int:

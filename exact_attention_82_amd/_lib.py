@@ -24,6 +24,7 @@ SIGNATURES = {
     "attn_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                              _i, _i, _vp]),
     "attn_splitkv_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "attn_splitkv_num_splits": (_i, [_i, _i, _i, _i, _i, _i]),
     "attn_fwd_splitkv": (_i, [_vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _i, _i, _f, _i, _i,
                               _f, _f, _f, _vp]),
     "attn_merge": (_i, [_vp, _sz, _i, _vp, _vp, _i, _i, _i, _i, _vp]),

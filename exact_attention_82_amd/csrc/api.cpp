@@ -120,6 +120,11 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, float* 
   return launched(attn::launch_fwd(a, stream));
 }
 
+int attn_splitkv_num_splits(int B, int H, int Sq, int Sk, int d, attn_dtype dtype) {
+  if (check_shape(B, H, Sq, Sk, d, dtype) != ATTN_OK) return 0;
+  return attn::splitkv_count(B, H, Sq, Sk, attn::device_cu_count());
+}
+
 size_t attn_splitkv_workspace_bytes(int B, int H, int Sq, int d, int num_splits) {
   if (B < 1 || H < 1 || Sq < 1 || !supported_d(d)) return 0;
   if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return 0;

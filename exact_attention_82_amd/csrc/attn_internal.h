@@ -101,6 +101,25 @@ inline FwdPlan plan_fwd(int B, int H, int Sq, int d, int causal, int dtype, int 
   return pl;
 }
 
+// Split count for attn_fwd_splitkv chosen from the shape.  The split-K section of "AI
+// 大模型之 FlashAttention_02" (interface and implementation constraints) notes that a
+// split adds a state write-back and a second launch, so short sequences may not gain,
+// and that the choice should follow the actual shape rather than the SM count alone.
+// Rule: 1 when the unsplit grid already gives every CU a workgroup or the keys are too
+// few; else the largest power of two n <= kMaxAutoSplits with B*H*ceil(Sq/128)*n <= CUs
+// (one workgroup per CU: the two-group kernel) and chunks of >= kMinSplitKeys keys.
+// Measured at B=1, H=8, Sq=128, Sk=32768, d=128 fp8 (8 query tiles): n = 16 / 32 / 64
+// take 44.5 / 39.0 / 45.6 us with the merge; the rule picks 32.
+constexpr int kMinSplitKeys = 1024;
+constexpr int kMaxAutoSplits = 64;
+inline int splitkv_count(int B, int H, int Sq, int Sk, int cus) {
+  const long long base = (long long)B * H * ((Sq + kBlockM - 1) / kBlockM);
+  if (cus <= 0 || base >= cus) return 1;
+  int n = 1;
+  while (2 * n <= kMaxAutoSplits && base * 2 * n <= cus && (long long)Sk >= 2LL * n * kMinSplitKeys) n *= 2;
+  return n;
+}
+
 struct MergeArgs {
   const float* ws_m;
   const float* ws_l;

@@ -131,6 +131,18 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, float* 
 size_t attn_splitkv_workspace_bytes(int B, int H, int Sq, int d, int num_splits);
 
 /*
+ * attn_splitkv_num_splits -- a split count for attn_fwd_splitkv chosen from the shape
+ * (the split-K section of "AI 大模型之 FlashAttention_02" asks for a choice that follows
+ * the shape, since the extra state write-back and merge launch can cancel the gain for
+ * short sequences).  Returns 1 when splitting does not pay -- the unsplit grid of
+ * B*H*ceil(Sq/128) workgroups already covers the device's CUs, or Sk < 2048 -- else the
+ * largest power of two n <= 64 that keeps B*H*ceil(Sq/128)*n within the CU count and every
+ * chunk at >= 1024 keys.  Depends on the current device's CU count (a cached HIP query;
+ * 1 without a device).  0 if an argument is out of range (as attn_fwd would refuse it).
+ */
+int attn_splitkv_num_splits(int B, int H, int Sq, int Sk, int d, attn_dtype dtype);
+
+/*
  * attn_fwd_splitkv -- local softmax states of an n-way split of the keys.
  *
  * The key axis is cut into n chunks of C = ceil(Sk / n) keys: chunk s covers keys

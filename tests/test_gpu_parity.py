@@ -192,8 +192,11 @@ def test_config4_sweep(d, S, B, causal):
 
 
 # ------------------------------------------------------------------ config 5: fp8 split-KV
-@pytest.mark.parametrize("n", [1, 4, 16])
+@pytest.mark.parametrize("n", [1, 4, 16, "auto"])
 def test_config5_fp8_splitkv(n):
+    if n == "auto":  # the count attn_splitkv_num_splits picks for this shape (32 on 256 CUs)
+        n = ea.attn_splitkv_num_splits(1, 8, 128, 32768, 128, ea.ATTN_FP8_E4M3)
+        assert n >= 1
     inp = si.make_attention_inputs(1, 8, 128, 32768, 128, seed=5, dtype="fp8")
     sc = scale_for(128)
     ws, o, lse = _run_split(inp, sc, False, n, descales=inp.scales)

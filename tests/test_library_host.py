@@ -85,6 +85,15 @@ def test_attn_fwd_varlen_refuses_bad_arguments(lib, kw, status):
     assert varlen(lib, **kw) == status
 
 
+def test_split_count_query(lib):
+    # out-of-range arguments give 0; without a GPU the CU count is unknown and the rule
+    # never splits (the split choice itself is tested in test_plan_host.py)
+    assert lib.attn_splitkv_num_splits(0, 8, 128, 32768, 128, 2) == 0
+    assert lib.attn_splitkv_num_splits(1, 8, 128, 32768, 96, 2) == 0
+    assert lib.attn_splitkv_num_splits(1, 8, 128, 32768, 128, 7) == 0
+    assert lib.attn_splitkv_num_splits(1, 8, 128, 32768, 128, 2) >= 1
+
+
 def test_splitkv_and_merge_refuse_bad_arguments(lib):
     need = lib.attn_splitkv_workspace_bytes(1, 2, 16, 64, 4)
     W = 0x60000

@@ -69,3 +69,32 @@ def test_head_group_divides_heads_and_fits_an_xcd(probe):
         (_, _, g), = probe([(1, bh, nqt * 128, 64, 0, BF16, 1)])
         assert bh % g == 0 and (g == 1 or g * nqt <= 64)
         assert not (bh % (2 * g) == 0 and 2 * g * nqt <= 64)   # largest such power of two
+
+
+@pytest.fixture(scope="module")
+def split_probe(tmp_path_factory):
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    exe = str(tmp_path_factory.mktemp("split") / "split_probe")
+    subprocess.run([cxx, "-std=c++17", "-O1", os.path.join(HERE, "split_probe.cpp"), "-o", exe], check=True)
+
+    def run(cases):
+        text = "".join(" ".join(str(x) for x in c) + "\n" for c in cases)
+        out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True).stdout
+        return [int(v) for v in out.split()]
+    return run
+
+
+def test_split_count_follows_the_shape(split_probe):
+    out = split_probe([
+        (1, 8, 128, 32768, 256),   # the fp8 split workload: 8 query tiles -> 32 chunks of 1024 keys
+        (8, 32, 2048, 2048, 256),  # 4096 workgroups unsplit: no split
+        (1, 8, 128, 1500, 256),    # too few keys for two chunks of >= 1024
+        (1, 8, 128, 4096, 256),    # chunks of >= 1024 keys cap the count at 4
+        (1, 100, 128, 1 << 20, 256),  # 100 tiles: only 2 fit the 256 CUs
+        (1, 1, 128, 1 << 20, 256),    # one tile: capped at 64 chunks
+        (1, 8, 128, 32768, 0),     # no device: no split
+        (1, 8, 128, 32768, 304),   # more CUs, same shape: still a power of two within the CUs
+    ])
+    assert out == [32, 1, 1, 4, 2, 64, 1, 32]
