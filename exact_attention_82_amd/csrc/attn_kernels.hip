@@ -730,8 +730,10 @@ template <int DT, int D, int BN, int NW> struct Pipe<DT, D, BN, NW, true> {
   static constexpr int STAGE_K = G::TILE, STAGE_V = G::TILE;
   static constexpr int NSTAGE = 4;
   static constexpr int KSTEPS = D / Traits<DT>::kKS;
-  // Operands go LDS -> registers ahead of their MFMAs where the registers allow it.
-  static constexpr bool kRegOps = DT == DT_BF16 && D <= 128;
+  // bf16 operands go LDS -> registers ahead of their MFMAs (d = 256 too: one wavefront
+  // per SIMD has 512 registers, and the deferred sweep's independent MFMA and VALU work
+  // is what overlaps there, +4-6 % measured).
+  static constexpr bool kRegOps = DT == DT_BF16;
   // Wait until at most N iterations' worth of tile loads are still in flight.
   static constexpr int NI = G::TILE / 1024 / NW;  // 1 KiB loads per wavefront per tile
   template <int N> __device__ __forceinline__ static void wait_loads() {
