@@ -124,9 +124,14 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, float* 
  *
  * Workspace layout (all fp32, each section starting at a multiple of 256 bytes from
  * the workspace base), with R = B*H*Sq rows and n = num_splits:
- *     m [n][B][H][Sq]   chunk maximum of the scaled scores, natural-log units (-inf: empty)
+ *     m [n][B][H][Sq]   the chunk's softmax reference in natural-log units (-inf: empty)
  *     l [n][B][H][Sq]   sum over the chunk of exp(S - m)
  *     u [n][B][H][Sq][d] sum over the chunk of exp(S - m) * v * v_descale (not divided by l)
+ * A chunk state is defined up to its reference: (m + t, l e^-t, u e^-t) is the same state
+ * and merges to the same result.  m is the chunk maximum of the scaled scores or lags it
+ * (the kernel moves its reference lazily: by at most 0.75 ln 2 for FP8 inputs, a bounded
+ * amount for the others); m + ln l (the chunk's log-sum-exp) and u / l (its normalised
+ * weighted average) do not depend on that choice.
  */
 size_t attn_splitkv_workspace_bytes(int B, int H, int Sq, int d, int num_splits);
 

@@ -202,13 +202,17 @@ def test_config5_fp8_splitkv(n):
     ws, o, lse = _run_split(inp, sc, False, n, descales=inp.scales)
     ro, rl = oracle.attention(inp.q64, inp.k64, inp.v64, sc, False)
     check(f"c5 fp8 n={n}", o, lse, ro, rl, "fp8")
-    # the chunk states themselves against the oracle's split states (head 0, a few rows)
+    # the chunk states themselves against the oracle's split states (head 0, a few rows).
+    # A state (m, l, u) is defined up to its reference: (m + t, l e^-t, u e^-t) merges the
+    # same way, and the kernel's reference may lag the chunk maximum; what is fixed is the
+    # chunk's log-sum-exp m + ln l and its normalised average u / l.
     m, l, u = (_np(t) for t in ea.workspace_views(ws, n, 1, 8, 128, 128))
     states = oracle.split_states(inp.q64[0, 0, :4], inp.k64[0, 0], inp.v64[0, 0], sc, n)
     for s, (sm, sl, su) in enumerate(states):
-        np.testing.assert_allclose(m[s, 0, 0, :4], sm, atol=1e-4)
-        np.testing.assert_allclose(l[s, 0, 0, :4] / sl, 1.0, atol=1e-4)
-        np.testing.assert_allclose(u[s, 0, 0, :4] / sl[:, None], su / sl[:, None], atol=5e-2)
+        mg, lg, ug = m[s, 0, 0, :4].astype(np.float64), l[s, 0, 0, :4], u[s, 0, 0, :4]
+        assert np.all(mg >= sm - 0.75 * math.log(2) - 1e-4) and np.all(mg <= sm + 1e-4)
+        np.testing.assert_allclose(mg + np.log(lg), sm + np.log(sl), atol=1e-3)
+        np.testing.assert_allclose(ug / lg[:, None], su / sl[:, None], atol=5e-2)
 
 
 def test_config5_fp8_direct_forward_with_folded_descales():
