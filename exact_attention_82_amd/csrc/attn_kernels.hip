@@ -1097,14 +1097,15 @@ void attn_fwd_kernel(FwdArgs p) {
       const bool act0 = ntiles > 0 && active(kbeg);
       if (act0) pipe.qk(sa, kst(0), qop);
       if (ntiles > 1 && active(kbeg + BN)) pipe.qk(sb, kst(1), qop);
-      if (act0) {
-        if (needs_mask(kbeg)) mask_tile<BN>(sa, kbeg, kend, row, off, p.causal, g);
-        softmax_tile<DT, BN, NDB>(sa, pa, oacc, m_run, l_run, c_run, sl2);
-      }
       block_sync();  // key tile 0's stage is free again
       if (ntiles > 0) {
         pipe.issue_k(rk, kbeg + 4 * BN, kst(0));
         pipe.issue_v(rv, kbeg + 2 * BN, vst(2));
+      }
+      // tile 0's softmax (registers only) while key tile 2 and value tile 0 land
+      if (act0) {
+        if (needs_mask(kbeg)) mask_tile<BN>(sa, kbeg, kend, row, off, p.causal, g);
+        softmax_tile<DT, BN, NDB>(sa, pa, oacc, m_run, l_run, c_run, sl2);
       }
       P::template wait_loads<2>();  // key tile 2 and value tile 0
       block_sync();
