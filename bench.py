@@ -274,6 +274,37 @@ def sweep(name: str, reps: int, warmup: int):
             del q, k, v, o, lse
             torch.cuda.empty_cache()
         return
+    if name == "out16":
+        # O written as bf16 (attn_fwd_ex) against fp32 O (attn_fwd): c3, c2 and the
+        # HBM-bound c4 shapes at S=512, where O is most of the bytes.
+        for (B, H, S, d, seed) in ((1, 8, 8192, 128, 3), (8, 32, 2048, 64, 2), (8, 16, 512, 128, 441),
+                                   (8, 16, 512, 64, 341)):
+            inp = si.make_attention_inputs(B, H, S, S, d, seed=seed, dtype="bf16")
+            q, k, v = to_dev(inp)
+            del inp
+            scale = float(np.float32(1.0 / np.sqrt(d)))
+            o32 = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
+            o16 = torch.empty((B, H, S, d), dtype=torch.bfloat16, device=dev)
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+            for causal in (False, True):
+                f32 = lambda: ea.attn_fwd(q, k, v, scale=scale, causal=causal, out=o32, lse=lse)
+                f16 = lambda: ea.attn_fwd_ex(q, k, v, scale=scale, causal=causal, out_dtype=torch.bfloat16,
+                                             out=o16, lse=lse)
+                for _ in range(warmup):
+                    f32()
+                    f16()
+                torch.cuda.synchronize()
+                u32 = _timed_calls(f32, reps, flush)
+                u16 = _timed_calls(f16, reps, flush)
+                fl = 4.0 * B * H * S * S * d / (2.0 if causal else 1.0)
+                emit({"workload": "out16", "B": B, "H": H, "Sq": S, "Sk": S, "d": d, "dtype": "bf16",
+                      "causal": causal, "kernel": ea.attn_kernel_name(B, H, S, d, int(causal), ea.ATTN_BF16),
+                      "reps": reps, "fp32_out": _stats(u32), "bf16_out": _stats(u16),
+                      "tflops_fp32_out": round(fl / (float(np.median(u32)) * 1e-6) / 1e12, 2),
+                      "tflops_bf16_out": round(fl / (float(np.median(u16)) * 1e-6) / 1e12, 2)})
+            del q, k, v, o32, o16, lse
+            torch.cuda.empty_cache()
+        return
     if name == "varlen":
         # ragged batches: 16 sequences of 256..4096 tokens (uniform, seeded), H=16, bf16;
         # useful FLOPs = sum over sequences of 4*H*l^2*d (half causal).  The same batch
@@ -401,6 +432,14 @@ def summarize_sweep(path: str) -> str:
     """Markdown table of the JSON lines written by --sweep."""
     recs = [json.loads(l) for l in open(path) if l.strip().startswith("{")]
     out = []
+    if recs and recs[0]["workload"] == "out16":
+        out += ["| B | H | S | d | mask | kernel | fp32 O median us | bf16 O median us | fp32 O TFLOP/s | bf16 O TFLOP/s |",
+                "|---|---|---|---|---|---|---|---|---|---|"]
+        for r in recs:
+            out.append(f"| {r['B']} | {r['H']} | {r['Sq']} | {r['d']} | {'causal' if r['causal'] else 'full'} | "
+                       f"{r['kernel']} | {r['fp32_out']['median_us']} | {r['bf16_out']['median_us']} | "
+                       f"{r['tflops_fp32_out']} | {r['tflops_bf16_out']} |")
+        return "\n".join(out)
     if recs and recs[0]["workload"] == "varlen":
         out += ["| sequences | H | d | tokens | longest | mask | kernel | median us | TFLOP/s | % of 2500 | padded dense median us | padded dense TFLOP/s (useful) |",
                 "|---|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -445,7 +484,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
-    ap.add_argument("--sweep", choices=("c1", "c2", "c4", "c5", "bwd", "varlen"),
+    ap.add_argument("--sweep", choices=("c1", "c2", "c4", "c5", "bwd", "varlen", "out16"),
                     help="per-case timing of a parity workload (JSON lines)")
     ap.add_argument("--sweep-reps", type=int, default=30)
     ap.add_argument("--summarize-sweep", metavar="JSONL")

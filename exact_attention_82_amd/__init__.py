@@ -26,7 +26,7 @@ from . import _lib
 from ._lib import ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3, ATTN_MAX_SPLITS, AttnError  # noqa: F401
 
 __all__ = [
-    "attn_fwd", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_merge", "attn_splitkv_workspace_bytes",
+    "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_merge", "attn_splitkv_workspace_bytes",
     "attn_splitkv_num_splits",
     "attn_block_m", "attn_block_n", "attn_num_workgroups", "attn_kernel_name",
     "attn_status_string", "attn_last_hip_error", "dtype_code", "library_path", "AttnError",
@@ -87,6 +87,27 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None)
                               ctypes_ptr(lse), B, H, Sq, Sk, d, float(scale), int(causal), dt,
                               _stream(stream))
     _lib.check("attn_fwd", st)
+    return out, lse
+
+
+def attn_fwd_ex(q, k, v, scale=None, causal=False, out_dtype=torch.bfloat16, out=None, lse=None,
+                stream=None):
+    """attn_fwd with O written as ``out_dtype`` (torch.float32 or torch.bfloat16; bf16 is the
+    fp32 result rounded to nearest even at the write-back); lse is float32."""
+    B, H, Sq, Sk, d, dt = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    odt = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}.get(out_dtype)
+    if odt is None:
+        raise TypeError(f"unsupported output dtype {out_dtype}")
+    if out is None:
+        out = torch.empty((B, H, Sq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    st = _lib.load().attn_fwd_ex(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out),
+                                 ctypes_ptr(lse), B, H, Sq, Sk, d, float(scale), int(causal), dt,
+                                 odt, _stream(stream))
+    _lib.check("attn_fwd_ex", st)
     return out, lse
 
 

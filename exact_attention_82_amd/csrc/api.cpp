@@ -65,6 +65,12 @@ extern "C" {
 attn_status attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
                      int B, int H, int Sq, int Sk, int d, float scale, int causal,
                      attn_dtype dtype, void* stream) {
+  return attn_fwd_ex(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, dtype, ATTN_F32, stream);
+}
+
+attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Sq, int Sk, int d, float scale, int causal,
+                        attn_dtype dtype, attn_dtype out_dtype, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   attn_status st = check_shape(B, H, Sq, Sk, d, dtype);
   if (st != ATTN_OK) return st;
@@ -74,8 +80,11 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, float* o, floa
   const float sl2 = static_cast<float>(double(scale) * kLog2e);
   if (!positive_finite(sl2)) return ATTN_ERR_ARG;
 
+  if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+
   attn::FwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.q = q; a.k = k; a.v = v; a.o = static_cast<float*>(o); a.lse = lse;
+  a.o_bf16 = out_dtype == ATTN_BF16;
   a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
   a.dtype = dtype; a.causal = causal;
   a.num_splits = 1; a.chunk = Sk; a.split_mode = 0;

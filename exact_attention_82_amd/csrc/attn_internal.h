@@ -45,6 +45,9 @@ struct FwdArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int total_q, total_k;
+  // O written as bf16 (round to nearest even) instead of fp32: `o` then points at
+  // uint16 elements (plain modes only; the split workspace stays fp32).
+  int o_bf16;
 };
 
 // Launch plan of a forward call: query rows per workgroup and the causal schedule.

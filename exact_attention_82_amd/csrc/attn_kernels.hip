@@ -940,7 +940,7 @@ void attn_fwd_kernel(FwdArgs p) {
     p.q = reinterpret_cast<const uint8_t*>(p.q) + qrow * D * EB;
     p.k = reinterpret_cast<const uint8_t*>(p.k) + krow * D * EB;
     p.v = reinterpret_cast<const uint8_t*>(p.v) + krow * D * EB;
-    p.o += qrow * D;
+    p.o = p.o_bf16 ? reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(p.o) + qrow * D) : p.o + qrow * D;
     p.lse += qrow;
     p.Sq = q_len;
     p.Sk = k_len;
@@ -1359,6 +1359,21 @@ void attn_fwd_kernel(FwdArgs p) {
         p.ws_m[sidx] = l_tot > 0.0f ? m_run * kLn2 : -__builtin_inff();
         p.ws_l[sidx] = l_tot;
       }
+    }
+    if (!SPLIT && p.o_bf16) {
+      // the same fp32 values, rounded to bf16 (nearest even) and stored as 8 bytes
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      uint16_t* out16 = reinterpret_cast<uint16_t*>(p.o) + ridx * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          f32x4_t v4 = {oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2],
+                        oacc[db][4 * jj + 3]};
+          *reinterpret_cast<u32x2_t*>(out16 + db * 32 + jj * 8 + g * 4) =
+              __builtin_bit_cast(u32x2_t, __builtin_convertvector(v4 * sc, bf16x4_t));
+        }
+      return;
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

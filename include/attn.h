@@ -84,6 +84,18 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, float* o, floa
                      attn_dtype dtype, void* stream);
 
 /*
+ * attn_fwd_ex -- attn_fwd with a choice of output type for O.
+ *
+ * out_dtype ATTN_F32 is attn_fwd.  ATTN_BF16 writes O as bfloat16 bit patterns (uint16,
+ * [B,H,Sq,d]): the same fp32 values attn_fwd computes, each rounded to the nearest bf16
+ * (ties to even) at the write-back, which halves the bytes O takes.  lse stays fp32.
+ * Other output types return ATTN_ERR_UNSUPPORTED.  Everything else as for attn_fwd.
+ */
+attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Sq, int Sk, int d, float scale, int causal,
+                        attn_dtype dtype, attn_dtype out_dtype, void* stream);
+
+/*
  * attn_fwd_varlen -- attn_fwd over a ragged batch: B sequences of different lengths
  * packed without padding (variable-length sequences handled as ragged tensors, as the
  * page "Inside FlashAttention-3", section 7.2, lists for the production integration).

@@ -85,6 +85,18 @@ def test_attn_fwd_varlen_refuses_bad_arguments(lib, kw, status):
     assert varlen(lib, **kw) == status
 
 
+def test_attn_fwd_ex_output_types(lib):
+    def ex(out_dtype, **kw):
+        a = dict(q=Q, k=K, v=V, o=O, l=L)
+        a.update(kw)
+        return lib.attn_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["l"], 1, 1, 8, 8, 64, 0.125, 0, 1,
+                               out_dtype, None)
+    assert ex(2) == 4           # fp8 output: unsupported
+    assert ex(7) == 4
+    assert ex(1, o=None) == 1   # the usual checks come first
+    assert ex(1, o=O + 8) == 3
+
+
 def test_split_count_query(lib):
     # out-of-range arguments give 0; without a GPU the CU count is unknown and the rule
     # never splits (the split choice itself is tested in test_plan_host.py)
