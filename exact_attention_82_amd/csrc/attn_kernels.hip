@@ -623,19 +623,7 @@ __device__ __forceinline__ void softmax_sums(const f32x16_t (&s)[BN / 32], const
         }
     c_run += cs;
   } else if constexpr (DT == DT_FP8) {
-    float cs = 0.0f;
-#pragma unroll
-    for (int b = 0; b < BN / 32; ++b)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int v = (int)(uint32_t)((unsigned long)pt.pk[b][h] >> (32 * q));
-          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
-          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
-          cs += (lo[0] + lo[1]) + (hi[0] + hi[1]);
-        }
-    c_run += cs * (1.0f / TR::kPScale);
+    // the packed sum comes from fp8_psum (an MFMA), folded into c_run by the sweep
   } else {
     c_run += ls;
   }
@@ -684,6 +672,17 @@ __device__ __forceinline__ float softmax_redo(const f32x16_t (&s)[BN / 32], f32x
     m_run = m_new;
   }
   return softmax_exp_ref<BN>(s, p, m_run == -__builtin_inff() ? 0.0f : m_run, sl2);
+}
+
+// FP8: the column sums of a tile's packed probabilities (one per query, the same in every
+// accumulator element of the lane) from one 64-deep MFMA with an all-ones E4M3 block
+// (0x38 = 1.0) as the A operand: exact products, fp32 accumulation like the value MFMA.
+__device__ __forceinline__ f32x16_t fp8_psum(const PTile<DT_FP8, 64>& pt) {
+  const i32x8_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  const i32x8_t pb = __builtin_bit_cast(i32x8_t, (long __attribute__((ext_vector_type(4)))){
+      pt.pk[0][0], pt.pk[0][1], pt.pk[1][0], pt.pk[1][1]});
+  return Traits<DT_FP8>::mfma(ones, pb, f32x16_t{});
 }
 
 // Probabilities -> value-MFMA operands (bf16), and the sum of exactly those values.
@@ -1228,6 +1227,21 @@ void attn_fwd_kernel(FwdArgs p) {
     // O^T += V^T P^T with tile t's values.  Key tile t+NS and value tile t+NS-1 are
     // requested into the stages that iteration t-1 finished reading; at the end of
     // the iteration only the loads that iteration t+1 needs are waited for.
+    // FP8: each active tile's packed-probability sum is computed by fp8_psum after its
+    // value MFMAs and folded into c_run at the next step, before that step's possible
+    // rescale (c_run and the sum share the reference of the tile), so nothing waits on
+    // the MFMA.  Every lane holds its query's full sum; half of it goes to each of the
+    // two lanes whose partial sums pair_sum adds.
+    [[maybe_unused]] f32x16_t psum = {};
+    auto fold_psum = [&]() __attribute__((always_inline)) {
+      if constexpr (DT == DT_FP8) {
+        c_run += psum[0] * (0.5f / TR::kPScale);
+        psum[0] = 0.0f;
+      }
+    };
+    auto take_psum = [&](const PTile<DT, BN>& pt) __attribute__((always_inline)) {
+      if constexpr (DT == DT_FP8) psum = fp8_psum(pt);
+    };
     auto finish = [&](uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
       pipe.commit_k(kdst, gtid);
       pipe.commit_v(vdst, gtid);
@@ -1265,8 +1279,10 @@ void attn_fwd_kernel(FwdArgs p) {
         interleave_pv<D, BN>();
       } else {
         pipe.qk(s_next, kb, qop);
+        fold_psum();
         softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
         pipe.pv(oacc, s_cur, pt, vb);
+        take_psum(pt);
       }
       finish(kdst, vdst);
     };
@@ -1280,11 +1296,13 @@ void attn_fwd_kernel(FwdArgs p) {
       pipe.issue_k(rk, k0 + NS * BN, kdst);
       pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
       if (act_next) pipe.qk(s_next, kb, qop);
+      fold_psum();
       if (act_cur) {
         if (needs_mask(k0)) mask_tile<BN>(s_cur, k0, kend, row, off, p.causal, g);
         PTile<DT, BN> pt;
         softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
         pipe.pv(oacc, s_cur, pt, vb);
+        take_psum(pt);
       }
       finish(kdst, vdst);
     };
@@ -1329,6 +1347,7 @@ void attn_fwd_kernel(FwdArgs p) {
     };
     run(std::true_type{}, 0, nfull);
     run(std::false_type{}, nfull, ntiles);
+    fold_psum();  // the last tile's packed sum
     // Drain every load before the rings are reused, by this group or the next sweep.
     wait_vmem();
     block_sync();
