@@ -149,6 +149,34 @@ def summarize_traffic(fetch_dir: str, write_dir: str, probe_mib: int, workload: 
     ])
 
 
+def summarize_pmc(dirs) -> str:
+    """Markdown table of `rocprofv3 --pmc` counter runs (one directory per pass): the mean
+    per dispatch of every counter, for each attention kernel instance seen."""
+    acc = {}
+    for d in dirs:
+        per = {}
+        for r in _csv_rows(d, "_counter_collection.csv"):
+            if "attn_" not in r["Kernel_Name"]:
+                continue
+            key = (r["Kernel_Name"], r["Counter_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])  # sum over instances
+        for (k, c, _), v in per.items():
+            acc.setdefault((k, c), []).append(v)
+    dur = {}
+    for d in dirs:
+        for r in _csv_rows(d, "_kernel_trace.csv"):
+            if "attn_" in r["Kernel_Name"]:
+                dur.setdefault(r["Kernel_Name"], []).append(
+                    (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3)
+    short = lambda k: k.replace("void attn::(anonymous namespace)::", "").split("(attn::")[0]
+    out = ["| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
+    for k, us in sorted(dur.items()):
+        out.append(f"| {short(k)} | duration (us, counter runs) | {len(us)} | {np.mean(us):.1f} |")
+    for (k, c), vs in sorted(acc.items()):
+        out.append(f"| {short(k)} | {c} | {len(vs)} | {np.mean(vs):.6g} |")
+    return "\n".join(out)
+
+
 def cpu_baseline(inp, scale, budget_s: float, gpu_out):
     """The CPU leg: time the fp64 oracle on whole heads of the same workload, both masks,
     head after head (cycling through the heads), until the time budget is used; and, with
@@ -490,6 +518,8 @@ def main():
     ap.add_argument("--summarize-sweep", metavar="JSONL")
     ap.add_argument("--summarize-stats", metavar="DIR",
                     help="print a table of a rocprofv3 --stats output directory and exit")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="print per-kernel means of rocprofv3 --pmc counter runs and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print HBM bytes per launch from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
@@ -498,6 +528,9 @@ def main():
         return
     if args.summarize_sweep:
         print(summarize_sweep(args.summarize_sweep))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
         return
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic, probe_mib=args.copy_probe_mib or 512,
