@@ -1070,11 +1070,12 @@ void attn_fwd_kernel(FwdArgs p) {
     };
 
     if constexpr (kDeferred) {
-      // ---- deferred pipeline (bf16, d <= 128; not the causal pair mode, whose two sweeps
-      // per group pay the longer prologue twice: measured 2-5 % slower there).  Iteration t computes S^T of key tile
-      // t+2, adds P(t) V(t) with the probabilities packed in iteration t-1, and turns
-      // the scores of tile t+1 into P(t+1): none of the iteration's MFMAs waits for
-      // its own exponentials, so the two interleave freely.  Tile j's keys and values
+      // ---- deferred pipeline (bf16, every head dim; not the causal pair mode, whose two
+      // sweeps per group pay the longer prologue twice: measured 2-5 % slower there).
+      // Iteration t computes S^T of key tile t+2, adds P(t) V(t) with the probabilities
+      // packed in iteration t-1, and turns the scores of tile t+1 into P(t+1): none of
+      // the iteration's MFMAs waits for its own exponentials, so the two interleave
+      // freely.  Tile j's keys and values
       // live in stage j % 4; iteration t requests key tile t+5 (into the stage of key
       // tile t+1, read in iteration t-1) and value tile t+3 (into the stage of value
       // tile t-1).  In every iteration the newest two iterations' loads may stay in
