@@ -23,10 +23,12 @@ import math
 import torch
 
 from . import _lib
-from ._lib import ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3, ATTN_MAX_SPLITS, AttnError  # noqa: F401
+from ._lib import (ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3, ATTN_MAX_SPLITS,  # noqa: F401
+                   ATTN_NOALLOC_SCRATCH_BYTES, AttnError)
 
 __all__ = [
     "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_merge", "attn_splitkv_workspace_bytes",
+    "attn_fwd_splitkv_noalloc",
     "attn_splitkv_num_splits",
     "attn_block_m", "attn_block_n", "attn_num_workgroups", "attn_kernel_name",
     "attn_status_string", "attn_last_hip_error", "dtype_code", "library_path", "AttnError",
@@ -182,6 +184,27 @@ def attn_merge(ws, num_splits, B, H, Sq, d, out=None, lse=None, stream=None):
     st = _lib.load().attn_merge(ctypes_ptr(ws), ws.numel() * ws.element_size(), int(num_splits),
                                 ctypes_ptr(out), ctypes_ptr(lse), B, H, Sq, d, _stream(stream))
     _lib.check("attn_merge", st)
+    return out, lse
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, num_splits, scale=None, causal=False,
+                             descales=(1.0, 1.0, 1.0), out=None, lse=None, stream=None):
+    """attn_fwd_splitkv + attn_merge in one library call whose chunk states live in the
+    library's static device array (the C call allocates nothing; calls that overlap on one
+    GPU race).  Returns (O, lse), float32."""
+    B, H, Sq, Sk, d, dt = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Sq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    qd, kd, vd = (float(x) for x in descales)
+    st = _lib.load().attn_fwd_splitkv_noalloc(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v),
+                                              ctypes_ptr(out), ctypes_ptr(lse), int(num_splits),
+                                              B, H, Sq, Sk, d, float(scale), int(causal), dt,
+                                              qd, kd, vd, _stream(stream))
+    _lib.check("attn_fwd_splitkv_noalloc", st)
     return out, lse
 
 

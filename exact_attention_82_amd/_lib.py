@@ -15,6 +15,7 @@ STATUS = {
     4: "ATTN_ERR_UNSUPPORTED", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_ARG",
 }
 ATTN_MAX_SPLITS = 4096
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
@@ -29,6 +30,8 @@ SIGNATURES = {
     "attn_fwd_splitkv": (_i, [_vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _i, _i, _f, _i, _i,
                               _f, _f, _f, _vp]),
     "attn_merge": (_i, [_vp, _sz, _i, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "attn_fwd_splitkv_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i,
+                                      _f, _f, _f, _vp]),
     "attn_block_m": (_i, [_i, _i, _i, _i, _i, _i, _i]),
     "attn_block_n": (_i, [_i, _i]),
     "attn_num_workgroups": (ctypes.c_int64, [_i, _i, _i, _i, _i, _i, _i]),

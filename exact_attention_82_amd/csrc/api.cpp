@@ -50,6 +50,58 @@ int splitkv_schedule(int B, int H, int Sq, int d, int dtype, int num_splits) {
   return attn::dual_schedule(nwg, dtype, d, attn::device_cu_count());
 }
 
+// Checks shared by the split-KV entry points (all but the workspace); sl2 receives the
+// score factor scale * q_descale * k_descale * log2(e).
+attn_status check_splitkv(const void* q, const void* k, const void* v, int num_splits, int B,
+                          int H, int Sq, int Sk, int d, float scale, int causal, int dtype,
+                          float q_descale, float k_descale, float v_descale, float* sl2) {
+  attn_status st = check_shape(B, H, Sq, Sk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ATTN_ERR_ALIGN;
+  if ((causal != 0 && causal != 1) || !positive_finite(scale) || !positive_finite(q_descale) ||
+      !positive_finite(k_descale) || !positive_finite(v_descale))
+    return ATTN_ERR_ARG;
+  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
+  *sl2 = static_cast<float>(double(scale) * double(q_descale) * double(k_descale) * kLog2e);
+  if (!positive_finite(*sl2)) return ATTN_ERR_ARG;
+  return ATTN_OK;
+}
+
+// The split kernel writing chunk states into the workspace at ws (layout w).
+int launch_splitkv(const void* q, const void* k, const void* v, void* ws,
+                   const attn::WorkspaceLayout& w, int num_splits, int B, int H, int Sq, int Sk,
+                   int d, float sl2, int causal, int dtype, float v_descale, void* stream) {
+  char* base = static_cast<char*>(ws);
+  attn::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.ws_m = reinterpret_cast<float*>(base + w.m_off);
+  a.ws_l = reinterpret_cast<float*>(base + w.l_off);
+  a.ws_u = reinterpret_cast<float*>(base + w.u_off);
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.dtype = dtype; a.causal = causal;
+  a.num_splits = num_splits;
+  a.chunk = static_cast<int>(ceil_div(Sk, num_splits));
+  a.split_mode = 1;
+  a.scale_log2 = sl2;
+  a.v_scale = v_descale;
+  a.pair_order = splitkv_schedule(B, H, Sq, d, dtype, num_splits);
+  a.head_group = attn::head_group(int64_t(B) * H, int((Sq + attn::kBlockM - 1) / attn::kBlockM));
+  return attn::launch_fwd(a, stream);
+}
+
+// The merge kernel reading the chunk states at ws (layout w).
+int launch_merge_ws(const void* ws, const attn::WorkspaceLayout& w, int num_splits, float* o,
+                    float* lse, int64_t rows, int d, void* stream) {
+  const char* base = static_cast<const char*>(ws);
+  attn::MergeArgs a{};
+  a.ws_m = reinterpret_cast<const float*>(base + w.m_off);
+  a.ws_l = reinterpret_cast<const float*>(base + w.l_off);
+  a.ws_u = reinterpret_cast<const float*>(base + w.u_off);
+  a.o = o; a.lse = lse;
+  a.rows = rows; a.d = d; a.num_splits = num_splits;
+  return attn::launch_merge(a, stream);
+}
+
 attn_status launched(int hip_err) {
   if (hip_err != 0) {
     g_last_hip_error = hip_err;
@@ -148,36 +200,15 @@ attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v,
                              attn_dtype dtype, float q_descale, float k_descale,
                              float v_descale, void* stream) {
   if (!q || !k || !v || !ws) return ATTN_ERR_NULL;
-  attn_status st = check_shape(B, H, Sq, Sk, d, dtype);
+  float sl2 = 0.0f;
+  attn_status st = check_splitkv(q, k, v, num_splits, B, H, Sq, Sk, d, scale, causal, dtype,
+                                 q_descale, k_descale, v_descale, &sl2);
   if (st != ATTN_OK) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(ws)) return ATTN_ERR_ALIGN;
-  if ((causal != 0 && causal != 1) || !positive_finite(scale) || !positive_finite(q_descale) ||
-      !positive_finite(k_descale) || !positive_finite(v_descale))
-    return ATTN_ERR_ARG;
-  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
-  const float sl2 =
-      static_cast<float>(double(scale) * double(q_descale) * double(k_descale) * kLog2e);
-  if (!positive_finite(sl2)) return ATTN_ERR_ARG;
-  const int64_t rows = int64_t(B) * H * Sq;
-  const attn::WorkspaceLayout w = attn::workspace_layout(rows, d, num_splits);
+  if (!aligned16(ws)) return ATTN_ERR_ALIGN;
+  const attn::WorkspaceLayout w = attn::workspace_layout(int64_t(B) * H * Sq, d, num_splits);
   if (ws_bytes < w.total) return ATTN_ERR_WORKSPACE;
-
-  char* base = static_cast<char*>(ws);
-  attn::FwdArgs a{};
-  a.q = q; a.k = k; a.v = v;
-  a.ws_m = reinterpret_cast<float*>(base + w.m_off);
-  a.ws_l = reinterpret_cast<float*>(base + w.l_off);
-  a.ws_u = reinterpret_cast<float*>(base + w.u_off);
-  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
-  a.dtype = dtype; a.causal = causal;
-  a.num_splits = num_splits;
-  a.chunk = static_cast<int>(ceil_div(Sk, num_splits));
-  a.split_mode = 1;
-  a.scale_log2 = sl2;
-  a.v_scale = v_descale;
-  a.pair_order = splitkv_schedule(B, H, Sq, d, dtype, num_splits);
-  a.head_group = attn::head_group(int64_t(B) * H, int((Sq + attn::kBlockM - 1) / attn::kBlockM));
-  return launched(attn::launch_fwd(a, stream));
+  return launched(launch_splitkv(q, k, v, ws, w, num_splits, B, H, Sq, Sk, d, sl2, causal, dtype,
+                                 v_descale, stream));
 }
 
 attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o, float* lse,
@@ -191,15 +222,32 @@ attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o
   if (rows * d >= kMaxIndex) return ATTN_ERR_SHAPE;
   const attn::WorkspaceLayout w = attn::workspace_layout(rows, d, num_splits);
   if (ws_bytes < w.total) return ATTN_ERR_WORKSPACE;
+  return launched(launch_merge_ws(ws, w, num_splits, o, lse, rows, d, stream));
+}
 
-  const char* base = static_cast<const char*>(ws);
-  attn::MergeArgs a{};
-  a.ws_m = reinterpret_cast<const float*>(base + w.m_off);
-  a.ws_l = reinterpret_cast<const float*>(base + w.l_off);
-  a.ws_u = reinterpret_cast<const float*>(base + w.u_off);
-  a.o = o; a.lse = lse;
-  a.rows = rows; a.d = d; a.num_splits = num_splits;
-  return launched(attn::launch_merge(a, stream));
+attn_status attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, float* o,
+                                     float* lse, int num_splits, int B, int H, int Sq, int Sk,
+                                     int d, float scale, int causal, attn_dtype dtype,
+                                     float q_descale, float k_descale, float v_descale,
+                                     void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  float sl2 = 0.0f;
+  attn_status st = check_splitkv(q, k, v, num_splits, B, H, Sq, Sk, d, scale, causal, dtype,
+                                 q_descale, k_descale, v_descale, &sl2);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
+  const int64_t rows = int64_t(B) * H * Sq;
+  const attn::WorkspaceLayout w = attn::workspace_layout(rows, d, num_splits);
+  if (w.total > attn::kNoallocScratchBytes) return ATTN_ERR_WORKSPACE;
+  // The states of this call go to the GPU's static array: every entry is written by the
+  // split kernel before the merge reads it, so nothing needs clearing.
+  int err = 0;
+  void* ws = attn::noalloc_scratch(&err);
+  if (ws == nullptr) return launched(err != 0 ? err : 1);
+  st = launched(launch_splitkv(q, k, v, ws, w, num_splits, B, H, Sq, Sk, d, sl2, causal, dtype,
+                               v_descale, stream));
+  if (st != ATTN_OK) return st;
+  return launched(launch_merge_ws(ws, w, num_splits, o, lse, rows, d, stream));
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal) {

@@ -221,6 +221,11 @@ int launch_bwd(const BwdArgs& a, void* stream);
 const char* bwd_kernel_name(int d, int which);  // which: 0 prologue, 1 dK/dV, 2 dQ, 3 combine
 // Compute units of the current device (cached per device), or 0 if unknown.
 int device_cu_count();
+// Size of the static device array attn_fwd_splitkv_noalloc uses as its workspace, and
+// that array's address on the current device (looked up once per device; nullptr with
+// *hip_err set if the lookup fails).
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;  // ATTN_NOALLOC_SCRATCH_BYTES
+void* noalloc_scratch(int* hip_err);
 const char* fwd_kernel_name(int dtype, int d, int split_mode, int sched);
 
 }  // namespace attn

@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "attn_internal.h"
@@ -2064,6 +2065,37 @@ const char* bwd_kernel_name(int d, int which) {
       {"attn_bwd_pre_d256", "attn_bwd_dkdv_bf16_d256_bn128_bm32", "attn_bwd_dq_bf16_d256_bm128_bn32", "attn_bwd_combine_d256"}};
   if ((d != 64 && d != 128 && d != 256) || which < 0 || which > 3) return "";
   return names[d == 64 ? 0 : d == 128 ? 1 : 2][which];
+}
+
+// ------------------------------------------------------------------ static scratch
+// Workspace of attn_fwd_splitkv_noalloc (for callers that cannot allocate): a fixed
+// device array, one copy per GPU the library runs on, held until the process ends.  In
+// host code `scratch` names a host-side stand-in, never a device address: kernels get the
+// address hipGetSymbolAddress returns for the current device.
+__device__ __align__(256) static uint8_t scratch[kNoallocScratchBytes];
+
+void* noalloc_scratch(int* hip_err) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= 64)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    *hip_err = int(e);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // once per device, with that device current: its own copy of the array
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *hip_err = int(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
 }
 
 int device_cu_count() {

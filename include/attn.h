@@ -197,6 +197,34 @@ attn_status attn_merge(const void* ws, size_t ws_bytes, int num_splits, float* o
                        int B, int H, int Sq, int d, void* stream);
 
 /*
+ * attn_fwd_splitkv_noalloc -- attn_fwd_splitkv followed by attn_merge in one call, with
+ * the chunk states in a workspace the library owns: the call allocates nothing.
+ *
+ * For callers that cannot allocate device memory -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The workspace is a static device array
+ * of ATTN_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until the
+ * process ends; its address on a GPU is looked up once, on the first call with that GPU
+ * current.  Every state entry is written by the split launch before the merge launch
+ * reads it, so nothing is cleared between calls.
+ *
+ *   q, k, v, num_splits, B, H, Sq, Sk, d, scale, causal, dtype, descales
+ *                  as for attn_fwd_splitkv
+ *   o, lse         device pointers, fp32 outputs [B,H,Sq,d] and [B,H,Sq], as for attn_merge
+ * The result is that of attn_fwd_splitkv + attn_merge with the same arguments (the same
+ * two launches, on `stream`).  Returns ATTN_ERR_WORKSPACE, before anything is launched,
+ * when attn_splitkv_workspace_bytes(B, H, Sq, d, num_splits) exceeds
+ * ATTN_NOALLOC_SCRATCH_BYTES, and ATTN_ERR_HIP if the array's address cannot be found.
+ * Calls on one GPU share its one array: calls that overlap on the same GPU (other streams,
+ * other threads) race and give wrong results; calls ordered on one stream do not.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+attn_status attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, float* o,
+                                     float* lse, int num_splits, int B, int H, int Sq, int Sk,
+                                     int d, float scale, int causal, attn_dtype dtype,
+                                     float q_descale, float k_descale, float v_descale,
+                                     void* stream);
+
+/*
  * attn_bwd_workspace_bytes -- bytes of the workspace attn_bwd needs for this shape, or 0
  * if an argument is out of range.  Layout (each section at a multiple of 256 bytes from
  * the base), R = B*H*Sq rows: dO rounded to bf16 [R][d], D = sum_d dO*O [R] (fp32), lse

@@ -203,3 +203,25 @@ def test_backward_refuses_bad_arguments_and_lays_out_its_workspace(lib):
     names = {lib.attn_bwd_kernel_name(d, 1, w).decode() for w in range(3)}
     assert all(n.startswith("attn_bwd_") for n in names) and len(names) == 3
     assert lib.attn_bwd_kernel_name(d, 0, 1).decode() == "unsupported"
+
+
+def test_splitkv_noalloc_refuses_bad_arguments_before_any_device_call(lib):
+    """The allocation-free split call checks everything -- including that the workspace
+    fits the library's static device array -- before it looks the array up or launches."""
+    from exact_attention_82_amd import _lib
+
+    def call(o=O, l=L, n=4, B=1, H=2, Sq=16, Sk=64, d=64, dtype=2, qd=1.0, causal=0):
+        return lib.attn_fwd_splitkv_noalloc(Q, K, V, o, l, n, B, H, Sq, Sk, d, 0.125, causal, dtype,
+                                            qd, 1.0, 1.0, None)
+    assert call(o=None) == 1 and call(l=None) == 1
+    assert call(B=0) == 2
+    assert call(d=100) == 4 and call(dtype=9) == 4
+    assert call(o=O + 4) == 3 and call(l=L + 8) == 3
+    assert call(n=0) == 7 and call(n=4097) == 7 and call(qd=0.0) == 7 and call(causal=2) == 7
+    # 64 heads x 1024 rows x 64 chunks of (d + 2) floats: far beyond the static array
+    assert lib.attn_splitkv_workspace_bytes(1, 64, 1024, 128, 64) > _lib.ATTN_NOALLOC_SCRATCH_BYTES
+    assert call(H=64, Sq=1024, Sk=4096, d=128, n=64) == 5
+    # the fp8 split workload (B=1, H=8, Sq=128, d=128) fits up to 32 chunks, the count the
+    # split rule picks for it on a 256-CU device
+    assert lib.attn_splitkv_workspace_bytes(1, 8, 128, 128, 32) <= _lib.ATTN_NOALLOC_SCRATCH_BYTES
+    assert lib.attn_splitkv_workspace_bytes(1, 8, 128, 128, 64) > _lib.ATTN_NOALLOC_SCRATCH_BYTES
