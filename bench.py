@@ -16,7 +16,12 @@ Prints one JSON line.  Besides the headline throughput it carries
                 the bf16 dense MFMA peak; `traffic` is its HBM bytes per launch
                 measured by rocprofv3 counters (profiles/), or null when that
                 measurement does not match the current kernel source;
-  cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample.
+  cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample;
+  clock         the shader clock under the dominant kernel (sampled through amdsmi while
+                it runs back to back, outside the timed region), with the roofline
+                fraction also against the peak at that clock;
+  environment   GPU name / arch / CUs, ROCm, hipcc and torch versions, CPU model, host
+                cores, NumPy and its BLAS.
 With the CPU leg, a few sampled rows of two heads are also checked against the oracle's
 outputs (outside the timed region).
 
@@ -175,6 +180,115 @@ def summarize_pmc(dirs) -> str:
     for (k, c), vs in sorted(acc.items()):
         out.append(f"| {short(k)} | {c} | {len(vs)} | {np.mean(vs):.6g} |")
     return "\n".join(out)
+
+
+def _gfx_clock_sampler():
+    """A function returning (shader clock in MHz, graphics activity in %) of the GPU, read
+    through amdsmi from the SMU's metrics table (mean over the XCDs' clocks), and a
+    description of the source; (None, reason) if amdsmi cannot be used here.  Read-only
+    queries."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+    except Exception as e:  # noqa: BLE001
+        return None, f"amdsmi unavailable: {type(e).__name__}"
+    if not handles:
+        return None, "amdsmi lists no GPU"
+    vis = os.environ.get("HIP_VISIBLE_DEVICES") or os.environ.get("ROCR_VISIBLE_DEVICES") or "0"
+    idx = int(vis.split(",")[0]) if vis.split(",")[0].isdigit() else 0
+    h = handles[idx if idx < len(handles) else 0]
+
+    def num(x):
+        return float(x) if isinstance(x, (int, float)) and 0 < x < 10000 else None
+
+    def read():
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        except Exception:  # noqa: BLE001
+            return None, None
+        xs = [num(x) for x in (m.get("current_gfxclks") or [])]
+        xs = [x for x in xs if x is not None]
+        clk = float(np.mean(xs)) if xs else num(m.get("current_gfxclk"))
+        act = m.get("average_gfx_activity")
+        return clk, (float(act) if isinstance(act, (int, float)) else None)
+    return read, "amdsmi gpu_metrics current_gfxclks (mean over the XCDs)"
+
+
+def measure_clock(launch, torch, seconds: float = 2.5):
+    """The shader clock under the dominant kernel, taken outside the timed region: the
+    kernel is launched back to back for `seconds` while a host thread samples the SMU's
+    metrics table (refreshed about once a second); samples taken while the graphics
+    activity reads >= 50 % count.  Returns {"mhz": median, "samples": n, "source": ...}."""
+    import threading
+    read, src = _gfx_clock_sampler()
+    if read is None:
+        return {"mhz": None, "samples": 0, "source": src}
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            clk, act = read()
+            if clk is not None and act is not None and act >= 50.0:
+                samples.append(clk)
+            time.sleep(0.02)
+    launch()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            launch()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    return {"mhz": round(float(np.median(samples)), 1) if samples else None,
+            "samples": len(samples), "source": src}
+
+
+def environment(torch, dev) -> dict:
+    """Versions and hardware the measurement ran on (recorded beside the numbers)."""
+    import platform
+    import subprocess
+    env = {}
+    try:
+        pr = torch.cuda.get_device_properties(dev)
+        env["gpu"] = pr.name
+        env["gpu_arch"] = getattr(pr, "gcnArchName", None)
+        env["gpu_cus"] = pr.multi_processor_count
+    except Exception as e:  # noqa: BLE001
+        env["gpu"] = f"unknown ({type(e).__name__})"
+    env["torch"] = torch.__version__
+    env["torch_hip"] = getattr(torch.version, "hip", None)
+    try:
+        env["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
+                             timeout=30).stdout
+        env["hipcc"] = next((l.strip() for l in out.splitlines() if "version" in l.lower()), None)
+    except Exception:  # noqa: BLE001
+        env["hipcc"] = None
+    cpu = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    env["cpu"] = cpu or platform.processor()
+    env["host_cores"] = len(os.sched_getaffinity(0))
+    env["numpy"] = np.__version__
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {})
+        env["blas"] = f"{blas.get('name')} {blas.get('version')}".strip()
+    except Exception:  # noqa: BLE001
+        env["blas"] = None
+    return env
 
 
 def cpu_baseline(inp, scale, budget_s: float, gpu_out):
@@ -599,6 +713,12 @@ def main():
     kern_ms = float(np.mean(per_mode_ms[False]))
     achieved = flops[False] / (kern_ms * 1e-3) / 1e12
 
+    # shader clock under the dominant kernel and the software / hardware it ran on, both
+    # outside the timed region
+    clock = measure_clock(lambda: ea.attn_fwd(q, k, v, scale=scale, causal=False, out=o, lse=lse),
+                          torch)
+    env = environment(torch, dev)
+
     # outputs of both masks for the CPU leg's check, copied outside the timed region
     gpu_out = {}
     for c in modes:
@@ -645,7 +765,16 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
         },
+        "clock": clock,
+        "environment": env,
     }
+    if clock.get("mhz"):
+        # frac = (clock / 2.4 GHz) x (MFMA busy fraction at that clock): the peak assumes
+        # 256 CUs x 4096 bf16 FLOP per clock at 2.4 GHz
+        cus = env.get("gpu_cus") or 256
+        at_clock = cus * 4096 * clock["mhz"] * 1e6 / 1e12
+        result["roofline"]["peak_at_measured_clock"] = round(at_clock, 1)
+        result["roofline"]["frac_at_measured_clock"] = round(achieved / at_clock, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"], worst = cpu_baseline(inp, scale, args.cpu_budget, gpu_out)
         result["numerics_max_abs_err_sampled"] = worst

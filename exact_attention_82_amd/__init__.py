@@ -57,6 +57,24 @@ def ctypes_ptr(t: torch.Tensor) -> int:
     return t.data_ptr()
 
 
+def _out(name, t, shape, dtype, device):
+    """Check a caller-supplied output tensor before the call: the C ABI gets only a pointer,
+    so a tensor of the wrong type, size or device would be written past its end."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    return t
+
+
+def _same_device(device, **tensors):
+    for name, t in tensors.items():
+        if t.device != device:
+            raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
 def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -73,6 +91,7 @@ def _qkv(q, k, v):
     dt = dtype_code(q)
     if dtype_code(k) != dt or dtype_code(v) != dt:
         raise TypeError("q, k and v must share one dtype")
+    _same_device(q.device, k=k, v=v)
     return B, H, Sq, Sk, d, dt
 
 
@@ -85,6 +104,8 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None)
         out = torch.empty((B, H, Sq, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _out("out", out, (B, H, Sq, d), torch.float32, q.device)
+    _out("lse", lse, (B, H, Sq), torch.float32, q.device)
     st = _lib.load().attn_fwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out),
                               ctypes_ptr(lse), B, H, Sq, Sk, d, float(scale), int(causal), dt,
                               _stream(stream))
@@ -106,6 +127,8 @@ def attn_fwd_ex(q, k, v, scale=None, causal=False, out_dtype=torch.bfloat16, out
         out = torch.empty((B, H, Sq, d), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _out("out", out, (B, H, Sq, d), out_dtype, q.device)
+    _out("lse", lse, (B, H, Sq), torch.float32, q.device)
     st = _lib.load().attn_fwd_ex(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out),
                                  ctypes_ptr(lse), B, H, Sq, Sk, d, float(scale), int(causal), dt,
                                  odt, _stream(stream))
@@ -135,10 +158,13 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _same_device(q.device, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k)
     if out is None:
         out = torch.empty((H, total_q, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    _out("out", out, (H, total_q, d), torch.float32, q.device)
+    _out("lse", lse, (H, total_q), torch.float32, q.device)
     st = _lib.load().attn_fwd_varlen(
         ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out), ctypes_ptr(lse),
         ctypes_ptr(cu_seqlens_q), ctypes_ptr(cu_seqlens_k), B, H, int(max_seqlen_q),
@@ -165,6 +191,7 @@ def attn_fwd_splitkv(q, k, v, num_splits, scale=None, causal=False, descales=(1.
     need = attn_splitkv_workspace_bytes(B, H, Sq, d, num_splits)
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _same_device(q.device, ws=ws)
     qd, kd, vd = (float(x) for x in descales)
     st = _lib.load().attn_fwd_splitkv(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(ws),
                                       ws.numel() * ws.element_size(), int(num_splits), B, H, Sq,
@@ -181,6 +208,8 @@ def attn_merge(ws, num_splits, B, H, Sq, d, out=None, lse=None, stream=None):
         out = torch.empty((B, H, Sq, d), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    _out("out", out, (B, H, Sq, d), torch.float32, dev)
+    _out("lse", lse, (B, H, Sq), torch.float32, dev)
     st = _lib.load().attn_merge(ctypes_ptr(ws), ws.numel() * ws.element_size(), int(num_splits),
                                 ctypes_ptr(out), ctypes_ptr(lse), B, H, Sq, d, _stream(stream))
     _lib.check("attn_merge", st)
@@ -199,6 +228,8 @@ def attn_fwd_splitkv_noalloc(q, k, v, num_splits, scale=None, causal=False,
         out = torch.empty((B, H, Sq, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _out("out", out, (B, H, Sq, d), torch.float32, q.device)
+    _out("lse", lse, (B, H, Sq), torch.float32, q.device)
     qd, kd, vd = (float(x) for x in descales)
     st = _lib.load().attn_fwd_splitkv_noalloc(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v),
                                               ctypes_ptr(out), ctypes_ptr(lse), int(num_splits),
@@ -223,15 +254,20 @@ def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, 
         if tuple(t.shape) != shape or t.dtype != torch.float32:
             raise ValueError(f"{name} must be float32 {list(shape)}")
     dev = q.device
+    _same_device(dev, o=o, dout=dout, lse=lse)
     if dq is None:
         dq = torch.empty((B, H, Sq, d), dtype=torch.float32, device=dev)
     if dk is None:
         dk = torch.empty((B, H, Sk, d), dtype=torch.float32, device=dev)
     if dv is None:
         dv = torch.empty((B, H, Sk, d), dtype=torch.float32, device=dev)
+    _out("dq", dq, (B, H, Sq, d), torch.float32, dev)
+    _out("dk", dk, (B, H, Sk, d), torch.float32, dev)
+    _out("dv", dv, (B, H, Sk, d), torch.float32, dev)
     if ws is None:
         ws = torch.empty(max(attn_bwd_workspace_bytes(B, H, Sq, Sk, d, causal), 16), dtype=torch.uint8,
                          device=dev)
+    _same_device(dev, ws=ws)
     st = _lib.load().attn_bwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(o),
                               ctypes_ptr(dout), ctypes_ptr(lse), ctypes_ptr(dq), ctypes_ptr(dk),
                               ctypes_ptr(dv), ctypes_ptr(ws), ws.numel() * ws.element_size(),

@@ -23,13 +23,18 @@ bool positive_finite(float x) { return std::isfinite(x) && x > 0.0f; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Shape checks common to the forward entry points.
-attn_status check_shape(int B, int H, int Sq, int Sk, int d, int dtype) {
+// Shape checks common to the entry points; num_splits is the split count of a split-KV
+// call (1 otherwise), which multiplies the grid.
+attn_status check_shape(int B, int H, int Sq, int Sk, int d, int dtype, int num_splits = 1) {
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ATTN_ERR_SHAPE;
   if (!supported_d(d) || !supported_dtype(dtype)) return ATTN_ERR_UNSUPPORTED;
   const int64_t bh = int64_t(B) * H;
   if (bh * Sq * d >= kMaxIndex || bh * Sk * d >= kMaxIndex) return ATTN_ERR_SHAPE;
-  if (bh * ceil_div(Sq, attn::kBlockM) >= (int64_t(1) << 31) / ATTN_MAX_SPLITS) return ATTN_ERR_SHAPE;
+  // Workgroup indices are 32-bit: the forward grid (one workgroup per 128 query rows per
+  // (batch, head), times the split count) and the backward's (per 128 keys, at most twice
+  // that with split key tiles) must stay below 2^31.
+  const int64_t tiles = ceil_div(Sq > Sk ? Sq : Sk, attn::kBlockM);
+  if (bh * tiles * 2 * num_splits >= (int64_t(1) << 31)) return ATTN_ERR_SHAPE;
   // One (batch, head) slice is addressed with 32-bit byte offsets, including the tile
   // loads the key sweep issues past the end of the sequence (at most a few tiles).
   const int64_t eb = dtype == ATTN_F32 ? 4 : dtype == ATTN_BF16 ? 2 : 1;
@@ -57,11 +62,13 @@ attn_status check_splitkv(const void* q, const void* k, const void* v, int num_s
                           float q_descale, float k_descale, float v_descale, float* sl2) {
   attn_status st = check_shape(B, H, Sq, Sk, d, dtype);
   if (st != ATTN_OK) return st;
+  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
+  st = check_shape(B, H, Sq, Sk, d, dtype, num_splits);
+  if (st != ATTN_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ATTN_ERR_ALIGN;
   if ((causal != 0 && causal != 1) || !positive_finite(scale) || !positive_finite(q_descale) ||
       !positive_finite(k_descale) || !positive_finite(v_descale))
     return ATTN_ERR_ARG;
-  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
   *sl2 = static_cast<float>(double(scale) * double(q_descale) * double(k_descale) * kLog2e);
   if (!positive_finite(*sl2)) return ATTN_ERR_ARG;
   return ATTN_OK;

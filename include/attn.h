@@ -86,6 +86,10 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, float* o, floa
 /*
  * attn_fwd_ex -- attn_fwd with a choice of output type for O.
  *
+ * The pages fix O's type only for one workload (fp32); BF16 is the reduced type they list
+ * for the attention kernels next to FP8 ("Inside FlashAttention-3", section 7.3, BF16 / FP8
+ * support), here for the output, whose bytes it halves.
+ *
  * out_dtype ATTN_F32 is attn_fwd.  ATTN_BF16 writes O as bfloat16 bit patterns (uint16,
  * [B,H,Sq,d]): the same fp32 values attn_fwd computes, each rounded to the nearest bf16
  * (ties to even) at the write-back, which halves the bytes O takes.  lse stays fp32.
@@ -140,10 +144,14 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, float* 
  *     l [n][B][H][Sq]   sum over the chunk of exp(S - m)
  *     u [n][B][H][Sq][d] sum over the chunk of exp(S - m) * v * v_descale (not divided by l)
  * A chunk state is defined up to its reference: (m + t, l e^-t, u e^-t) is the same state
- * and merges to the same result.  m is the chunk maximum of the scaled scores or lags it
- * (the kernel moves its reference lazily: by at most 0.75 ln 2 for FP8 inputs, a bounded
- * amount for the others); m + ln l (the chunk's log-sum-exp) and u / l (its normalised
- * weighted average) do not depend on that choice.
+ * and merges to the same result.  m is the chunk maximum of the scaled scores or lags it:
+ * the kernel moves its reference lazily, so m >= max - lag with lag = 0.75 ln 2 for FP8
+ * inputs, 8 ln 2 for fp32 inputs and 33 ln 2 (about 22.9) for bf16 inputs (the bf16 key
+ * sweep re-references only when a probability would pass 2^33).  A chunk that fits one
+ * key tile stores its exact maximum.  m + ln l (the chunk's log-sum-exp) and u / l (its
+ * normalised weighted average) do not depend on that choice.  (The split-K section of
+ * "AI 大模型之 FlashAttention_02", engineering practice, asks the interface to state this
+ * local-statistics layout: axis, per-chunk ownership and merge operator.)
  */
 size_t attn_splitkv_workspace_bytes(int B, int H, int Sq, int d, int num_splits);
 
@@ -287,7 +295,9 @@ int attn_block_n(int d, attn_dtype dtype);
 int64_t attn_num_workgroups(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
                             int num_splits);
 
-/* Name of the kernel instance the call launches (static string; "unsupported" if none). */
+/* Name of the kernel instance the call launches (static string; "unsupported" if none):
+ * the real kernel name a measurement records with its software versions ("AI 大模型之
+ * FlashAttention_02", section "Experiment code and timing discipline"). */
 const char* attn_kernel_name(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
                              int num_splits);
 

@@ -3,7 +3,10 @@ evaluation on all or on sampled rows, and the tolerance check.
 
 Tolerances (from the stated parity bar): bf16 inputs max|dO| <= 1e-2 and mean|dO| <= 1e-3;
 fp32 inputs max|dO| <= 1e-5; fp8 inputs max|dO| <= 5e-2; lse within 1e-3 on finite
-entries, and -inf entries (rows with no visible key) must match exactly.
+entries, and -inf entries (rows with no visible key) must match exactly.  The bar states
+no mean for fp8; the one used here, 1e-2, is the max bar over 5: the E4M3 rounding of the
+probabilities (unit roundoff 2^-4) averages out over a row's keys, and the worst mean
+measured (ragged batches with a handful of keys per row) is about 3e-3.
 """
 import numpy as np
 import torch
@@ -13,7 +16,7 @@ import oracle
 TOL = {
     "f32": dict(max_o=1e-5, mean_o=1e-5, lse=1e-3),
     "bf16": dict(max_o=1e-2, mean_o=1e-3, lse=1e-3),
-    "fp8": dict(max_o=5e-2, mean_o=5e-2, lse=1e-3),
+    "fp8": dict(max_o=5e-2, mean_o=1e-2, lse=1e-3),
 }
 
 

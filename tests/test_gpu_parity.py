@@ -226,6 +226,12 @@ def test_config5_fp8_direct_forward_with_folded_descales():
 
 
 # ------------------------------------------------------------------ split-KV on other dtypes and masks
+# Largest lag (log2 units) of a stored chunk reference behind the chunk maximum: the bf16
+# main loop moves its reference only when a lane's probability sum would pass 2^33, the
+# guarded loop (and fp32) when a score passes the reference by 8.
+LAG_LOG2 = {"bf16": 33.0, "f32": 8.0}
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_splitkv_counts_with_empty_chunks(dtype, causal):
@@ -233,8 +239,30 @@ def test_splitkv_counts_with_empty_chunks(dtype, causal):
     sc = scale_for(128)
     ro, rl = oracle.attention(inp.q64, inp.k64, inp.v64, sc, causal)
     for n in (1, 2, 3, 4, 7, 16, 400):  # 400 > Sk: most chunks are empty
-        _, o, lse = _run_split(inp, sc, causal, n)
+        ws, o, lse = _run_split(inp, sc, causal, n)
         check(f"split {dtype} causal={causal} n={n}", o, lse, ro, rl, dtype)
+        # the chunk states of head (0, 0), every row, against the oracle's: empty or fully
+        # masked chunks are exactly neutral; otherwise the reference lies within the lag
+        # bound below the chunk maximum, and what does not depend on it -- the chunk's
+        # log-sum-exp m + ln l and its normalised average u / l -- matches.
+        m, l, u = (_np(t).astype(np.float64) for t in ea.workspace_views(ws, n, 2, 2, 150, 128))
+        states = oracle.split_states(inp.q64[0, 0], inp.k64[0, 0], inp.v64[0, 0], sc, n, causal)
+        tol_u = 1e-2 if dtype == "bf16" else 1e-5
+        for s, (sm, sl, su) in enumerate(states):
+            mg, lg, ug = m[s, 0, 0], l[s, 0, 0], u[s, 0, 0]
+            empty = np.isneginf(sm)
+            assert np.array_equal(np.isneginf(mg), empty), (n, s)
+            assert np.all(lg[empty] == 0.0) and np.all(ug[empty] == 0.0), (n, s)
+            full = ~empty
+            if not full.any():
+                continue
+            lag = LAG_LOG2[dtype] * math.log(2)
+            assert np.all(mg[full] <= sm[full] + 1e-4), (n, s)
+            assert np.all(mg[full] >= sm[full] - lag - 1e-4), (n, s)
+            np.testing.assert_allclose(mg[full] + np.log(lg[full]), sm[full] + np.log(sl[full]),
+                                       atol=1e-3)
+            np.testing.assert_allclose(ug[full] / lg[full, None], su[full] / sl[full, None],
+                                       atol=tol_u)
 
 
 # ------------------------------------------------------------------ causal schedules

@@ -225,3 +225,22 @@ def test_splitkv_noalloc_refuses_bad_arguments_before_any_device_call(lib):
     # split rule picks for it on a 256-CU device
     assert lib.attn_splitkv_workspace_bytes(1, 8, 128, 128, 32) <= _lib.ATTN_NOALLOC_SCRATCH_BYTES
     assert lib.attn_splitkv_workspace_bytes(1, 8, 128, 128, 64) > _lib.ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def test_grid_index_bound_follows_the_launch(lib):
+    """Workgroup indices are 32-bit.  Dense calls are bounded by their own grid, not by
+    the largest split grid: 8 x 64 heads of 131072 rows (2^19 workgroups, ~17 GB per
+    tensor) pass the shape checks; a split call is bounded with its actual split count."""
+    assert lib.attn_splitkv_num_splits(8, 64, 131072, 131072, 128, 1) >= 1
+    # 2 x 2^30 workgroup indices: refused
+    assert fwd(lib, B=1, H=65536, Sq=1 << 22, Sk=8, d=64) == 2
+    W = 0x60000
+
+    def split(n, nb=16):
+        return lib.attn_fwd_splitkv(Q, K, V, W, nb, n, 1, 512, 1 << 20, 64, 64, 0.125, 0, 1,
+                                    1.0, 1.0, 1.0, None)
+    # 512 heads x 8192 query tiles x n (x 2, the margin the checks keep for the backward's
+    # split key tiles): n = 256 reaches 2^31, n = 128 does not (it then fails on the
+    # 16-byte workspace instead)
+    assert split(256) == 2
+    assert split(128) == 5

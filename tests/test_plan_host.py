@@ -10,11 +10,19 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 BF16, FP8, F32 = 1, 2, 0
 
 
+def host_cxx():
+    """A host C++ compiler: g++ / c++, else ROCm's clang (the toolchain the library itself
+    needs), so that these checks run wherever the library can be built."""
+    for cand in (shutil.which("g++"), shutil.which("c++"), shutil.which("amdclang++"),
+                 "/opt/rocm/llvm/bin/clang++"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler (g++, c++ or ROCm clang++) for the plan probes")
+
+
 @pytest.fixture(scope="module")
 def probe(tmp_path_factory):
-    cxx = shutil.which("g++") or shutil.which("c++")
-    if cxx is None:
-        pytest.skip("no host C++ compiler")
+    cxx = host_cxx()
     exe = str(tmp_path_factory.mktemp("plan") / "plan_probe")
     subprocess.run([cxx, "-std=c++17", "-O1", os.path.join(HERE, "plan_probe.cpp"), "-o", exe], check=True)
 
@@ -73,9 +81,7 @@ def test_head_group_divides_heads_and_fits_an_xcd(probe):
 
 @pytest.fixture(scope="module")
 def split_probe(tmp_path_factory):
-    cxx = shutil.which("g++") or shutil.which("c++")
-    if cxx is None:
-        pytest.skip("no host C++ compiler")
+    cxx = host_cxx()
     exe = str(tmp_path_factory.mktemp("split") / "split_probe")
     subprocess.run([cxx, "-std=c++17", "-O1", os.path.join(HERE, "split_probe.cpp"), "-o", exe], check=True)
 
