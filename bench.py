@@ -402,7 +402,7 @@ def sweep(name: str, reps: int, warmup: int):
                 fl = 4.0 * B * H * S * S * d / (2.0 if causal else 1.0)
                 ab = _alg_bytes(B, H, S, S, d, in_bytes)
                 rec = {"workload": name, "B": B, "H": H, "Sq": S, "Sk": S, "d": d, "dtype": dt,
-                       "causal": causal, "kernel": ea.attn_kernel_name(B, H, S, d, int(causal),
+                       "causal": causal, "kernel": ea.attn_kernel_name(B, H, S, S, d, int(causal),
                                                                        ea.dtype_code(q)),
                        "reps": reps, **_stats(us)}
                 if dt != "f32":
@@ -440,7 +440,7 @@ def sweep(name: str, reps: int, warmup: int):
                 u16 = _timed_calls(f16, reps, flush)
                 fl = 4.0 * B * H * S * S * d / (2.0 if causal else 1.0)
                 emit({"workload": "out16", "B": B, "H": H, "Sq": S, "Sk": S, "d": d, "dtype": "bf16",
-                      "causal": causal, "kernel": ea.attn_kernel_name(B, H, S, d, int(causal), ea.ATTN_BF16),
+                      "causal": causal, "kernel": ea.attn_kernel_name(B, H, S, S, d, int(causal), ea.ATTN_BF16),
                       "reps": reps, "fp32_out": _stats(u32), "bf16_out": _stats(u16),
                       "tflops_fp32_out": round(fl / (float(np.median(u32)) * 1e-6) / 1e12, 2),
                       "tflops_bf16_out": round(fl / (float(np.median(u16)) * 1e-6) / 1e12, 2)})
@@ -481,7 +481,7 @@ def sweep(name: str, reps: int, warmup: int):
                 tf = fl / (float(np.median(us)) * 1e-6) / 1e12
                 emit({"workload": "varlen", "B": B, "H": H, "d": d, "dtype": "bf16", "causal": causal,
                       "lengths": [int(l) for l in lens], "total": T, "max_len": M,
-                      "kernel": ea.attn_kernel_name(1, H, M, d, 0, ea.ATTN_BF16), "reps": reps,
+                      "kernel": ea.attn_kernel_name(1, H, M, M, d, 0, ea.ATTN_BF16), "reps": reps,
                       **_stats(us), "tflops": round(tf, 2),
                       "pct_of_bound": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
                       "padded_dense": {**_stats(pus),
@@ -560,7 +560,7 @@ def sweep(name: str, reps: int, warmup: int):
             wsb = n * B * H * Sq * (d + 2) * 4
             t = float(np.median(u1)) + float(np.median(u2))
             emit({"workload": "c5", "B": B, "H": H, "Sq": Sq, "Sk": Sk, "d": d, "dtype": "fp8",
-                  "num_splits": n, "picked_by_attn_splitkv_num_splits": n == auto_n, "kernel": ea.attn_kernel_name(B, H, Sq, d, 0, ea.ATTN_FP8_E4M3, n),
+                  "num_splits": n, "picked_by_attn_splitkv_num_splits": n == auto_n, "kernel": ea.attn_kernel_name(B, H, Sq, Sk, d, 0, ea.ATTN_FP8_E4M3, n),
                   "reps": reps, "splitkv": _stats(u1), "merge": _stats(u2),
                   "total_us": round(t, 2), "alg_bytes": ab, "workspace_bytes_rw": 2 * wsb,
                   "alg_gbs": round(ab / (t * 1e-6) / 1e9, 1),
@@ -743,7 +743,7 @@ def main():
             "workload": f"{args.workload}: B={B}, H={H}, Sq=Sk={S}, d={d}, bf16 N(0,1) inputs, "
                         "fp32 O + lse; one step = non-causal + causal forward",
             "B": B, "H": H, "Sq": S, "Sk": S, "d": d, "masks": ["non-causal", "causal"],
-            "kernels": {m: ea.attn_kernel_name(B, H, S, d, c, ea.ATTN_BF16) for m, c in (("non_causal", 0), ("causal", 1))},
+            "kernels": {m: ea.attn_kernel_name(B, H, S, S, d, c, ea.ATTN_BF16) for m, c in (("non_causal", 0), ("causal", 1))},
         },
         "modes": {
             ("causal" if c else "non_causal"): {
@@ -757,7 +757,7 @@ def main():
             } for c in modes
         },
         "roofline": {
-            "kernel": ea.attn_kernel_name(B, H, S, d, 0, ea.ATTN_BF16),
+            "kernel": ea.attn_kernel_name(B, H, S, S, d, 0, ea.ATTN_BF16),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,

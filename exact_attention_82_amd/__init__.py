@@ -18,6 +18,7 @@ float32.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 
 import torch
@@ -31,6 +32,7 @@ __all__ = [
     "attn_fwd_splitkv_noalloc",
     "attn_splitkv_num_splits",
     "attn_block_m", "attn_block_n", "attn_num_workgroups", "attn_kernel_name",
+    "attn_tune", "attn_tune_splitkv", "attn_plan_get", "attn_plan_set", "attn_plan_clear", "plan_parts",
     "attn_status_string", "attn_last_hip_error", "dtype_code", "library_path", "AttnError",
 ]
 
@@ -294,20 +296,79 @@ def workspace_views(ws, num_splits, B, H, Sq, d):
     return m, l, u
 
 
-def attn_block_m(B, H, Sq, d, causal, dtype, num_splits=0):
-    return int(_lib.load().attn_block_m(B, H, Sq, d, int(causal), dtype, num_splits))
+def attn_block_m(B, H, Sq, Sk, d, causal, dtype, num_splits=0):
+    return int(_lib.load().attn_block_m(B, H, Sq, Sk, d, int(causal), dtype, num_splits))
 
 
 def attn_block_n(d, dtype):
     return int(_lib.load().attn_block_n(d, dtype))
 
 
-def attn_num_workgroups(B, H, Sq, d, causal, dtype, num_splits=0):
-    return int(_lib.load().attn_num_workgroups(B, H, Sq, d, int(causal), dtype, num_splits))
+def attn_num_workgroups(B, H, Sq, Sk, d, causal, dtype, num_splits=0):
+    return int(_lib.load().attn_num_workgroups(B, H, Sq, Sk, d, int(causal), dtype, num_splits))
 
 
-def attn_kernel_name(B, H, Sq, d, causal, dtype, num_splits=0):
-    return _lib.load().attn_kernel_name(B, H, Sq, d, int(causal), dtype, num_splits).decode()
+def attn_kernel_name(B, H, Sq, Sk, d, causal, dtype, num_splits=0):
+    return _lib.load().attn_kernel_name(B, H, Sq, Sk, d, int(causal), dtype, num_splits).decode()
+
+
+def attn_tune(q, k, v, scale=None, causal=False, reps=10, out=None, lse=None, stream=None):
+    """Time every legal launch plan of attn_fwd for this shape (synchronous), keep the best
+    for later attn_fwd calls with the same shape; returns the plan id."""
+    B, H, Sq, Sk, d, dt = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Sq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _out("out", out, (B, H, Sq, d), torch.float32, q.device)
+    _out("lse", lse, (B, H, Sq), torch.float32, q.device)
+    plan = ctypes.c_int(-1)
+    st = _lib.load().attn_tune(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out),
+                               ctypes_ptr(lse), B, H, Sq, Sk, d, float(scale), int(causal), dt,
+                               int(reps), ctypes.byref(plan), _stream(stream))
+    _lib.check("attn_tune", st)
+    return plan.value
+
+
+def attn_tune_splitkv(q, k, v, scale=None, causal=False, descales=(1.0, 1.0, 1.0), reps=10,
+                      out=None, lse=None, stream=None):
+    """Time split counts 1..64 of the split path (synchronous) and keep the best for
+    attn_splitkv_num_splits; returns the count."""
+    B, H, Sq, Sk, d, dt = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Sq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _out("out", out, (B, H, Sq, d), torch.float32, q.device)
+    _out("lse", lse, (B, H, Sq), torch.float32, q.device)
+    n = ctypes.c_int(-1)
+    qd, kd, vd = (float(x) for x in descales)
+    st = _lib.load().attn_tune_splitkv(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out),
+                                       ctypes_ptr(lse), B, H, Sq, Sk, d, float(scale), int(causal),
+                                       dt, qd, kd, vd, int(reps), ctypes.byref(n), _stream(stream))
+    _lib.check("attn_tune_splitkv", st)
+    return n.value
+
+
+def attn_plan_get(B, H, Sq, Sk, d, causal, dtype) -> int:
+    return int(_lib.load().attn_plan_get(B, H, Sq, Sk, d, int(causal), dtype))
+
+
+def attn_plan_set(B, H, Sq, Sk, d, causal, dtype, plan) -> None:
+    _lib.check("attn_plan_set", _lib.load().attn_plan_set(B, H, Sq, Sk, d, int(causal), dtype, int(plan)))
+
+
+def attn_plan_clear() -> None:
+    _lib.load().attn_plan_clear()
+
+
+def plan_parts(plan: int):
+    """(schedule, head_group) of a plan id."""
+    return plan & 3, 1 << (plan >> 2)
 
 
 def attn_status_string(status):

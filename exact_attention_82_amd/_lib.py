@@ -32,10 +32,17 @@ SIGNATURES = {
     "attn_merge": (_i, [_vp, _sz, _i, _vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_fwd_splitkv_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i,
                                       _f, _f, _f, _vp]),
-    "attn_block_m": (_i, [_i, _i, _i, _i, _i, _i, _i]),
+    "attn_block_m": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "attn_block_n": (_i, [_i, _i]),
-    "attn_num_workgroups": (ctypes.c_int64, [_i, _i, _i, _i, _i, _i, _i]),
-    "attn_kernel_name": (ctypes.c_char_p, [_i, _i, _i, _i, _i, _i, _i]),
+    "attn_num_workgroups": (ctypes.c_int64, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "attn_kernel_name": (ctypes.c_char_p, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "attn_tune": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i,
+                       ctypes.POINTER(_i), _vp]),
+    "attn_tune_splitkv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _f, _f,
+                               _f, _i, ctypes.POINTER(_i), _vp]),
+    "attn_plan_get": (_i, [_i, _i, _i, _i, _i, _i, _i]),
+    "attn_plan_set": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "attn_plan_clear": (None, []),
     "attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _i,
                       _f, _i, _i, _vp]),

@@ -2,8 +2,16 @@
 //
 // Every check runs before anything is launched, so a refused call has no effect on the
 // outputs and makes no HIP call.  The launches live in attn_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
 
 #include "../../include/attn.h"
 #include "attn_internal.h"
@@ -43,9 +51,50 @@ attn_status check_shape(int B, int H, int Sq, int Sk, int d, int dtype, int num_
   return ATTN_OK;
 }
 
-// Kernel plan of attn_fwd; it depends on the device's CU count (a cached HIP query).
-attn::FwdPlan plan_for(int B, int H, int Sq, int d, int causal, int dtype) {
-  return attn::plan_fwd(B, H, Sq, d, causal, dtype, attn::device_cu_count());
+// ---- plans chosen by attn_tune / attn_tune_splitkv, keyed by the full shape and the device
+struct PlanKey {
+  int dev, cus, dtype, d, causal, B, H, Sq, Sk;
+  bool operator<(const PlanKey& o) const {
+    return std::tie(dev, cus, dtype, d, causal, B, H, Sq, Sk) <
+           std::tie(o.dev, o.cus, o.dtype, o.d, o.causal, o.B, o.H, o.Sq, o.Sk);
+  }
+};
+std::mutex g_plan_mu;
+std::map<PlanKey, int> g_plans;         // attn_fwd plan ids
+std::map<PlanKey, int> g_split_counts;  // attn_fwd_splitkv chunk counts (causal = -1)
+std::atomic<int> g_tuned{0};            // entries in either map (0: no lookup at all)
+
+PlanKey plan_key(int B, int H, int Sq, int Sk, int d, int causal, int dtype) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  return PlanKey{dev, attn::device_cu_count(), dtype, d, causal, B, H, Sq, Sk};
+}
+
+attn::FwdPlan plan_of_id(int plan, int B, int H, int Sq) {
+  const int s = attn::plan_sched(plan);
+  (void)B; (void)H; (void)Sq;
+  return attn::FwdPlan{s == 2 ? 2 * attn::kBlockM : attn::kBlockM, s, attn::plan_head_group(plan)};
+}
+
+// Plan id attn_fwd uses for this call: the tuned one if attn_tune (or attn_plan_set) stored
+// one for this shape on this device, else the fixed rule's.
+int plan_id_for(int B, int H, int Sq, int Sk, int d, int causal, int dtype) {
+  if (g_tuned.load(std::memory_order_acquire) > 0) {
+    const PlanKey key = plan_key(B, H, Sq, Sk, d, causal, dtype);
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    auto it = g_plans.find(key);
+    if (it != g_plans.end()) return it->second;
+  }
+  return attn::default_plan(B, H, Sq, d, causal, dtype, attn::device_cu_count());
+}
+
+// Kernel plan of attn_fwd; it depends on the device's CU count (a cached HIP query) and on
+// a tuned choice for the shape, if any.
+attn::FwdPlan plan_for(int B, int H, int Sq, int Sk, int d, int causal, int dtype) {
+  const int id = plan_id_for(B, H, Sq, Sk, d, causal, dtype);
+  attn::FwdPlan pl = plan_of_id(id, B, H, Sq);
+  if (pl.pair_order == 1 || pl.pair_order == 2) pl.head_group = 1;
+  return pl;
 }
 
 // Schedule of attn_fwd_splitkv: the two-group kernel when the grid has at most one
@@ -72,6 +121,73 @@ attn_status check_splitkv(const void* q, const void* k, const void* v, int num_s
   *sl2 = static_cast<float>(double(scale) * double(q_descale) * double(k_descale) * kLog2e);
   if (!positive_finite(*sl2)) return ATTN_ERR_ARG;
   return ATTN_OK;
+}
+
+// The dense forward with a given plan.
+int launch_dense(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int Sq, int Sk, int d, float sl2, int causal, int dtype, bool o_bf16,
+                 const attn::FwdPlan& pl, void* stream) {
+  attn::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = static_cast<float*>(o); a.lse = lse;
+  a.o_bf16 = o_bf16;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.dtype = dtype; a.causal = causal;
+  a.num_splits = 1; a.chunk = Sk; a.split_mode = 0;
+  a.scale_log2 = sl2;
+  a.v_scale = 1.0f;
+  a.pair_order = pl.pair_order;
+  a.head_group = pl.head_group;
+  return attn::launch_fwd(a, stream);
+}
+
+// Checks of a dense forward call (attn_fwd, attn_tune); sl2 receives scale * log2(e).
+attn_status check_dense(const void* q, const void* k, const void* v, const void* o,
+                        const void* lse, int B, int H, int Sq, int Sk, int d, float scale,
+                        int causal, int dtype, float* sl2) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  attn_status st = check_shape(B, H, Sq, Sk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  if ((causal != 0 && causal != 1) || !positive_finite(scale)) return ATTN_ERR_ARG;
+  *sl2 = static_cast<float>(double(scale) * kLog2e);
+  if (!positive_finite(*sl2)) return ATTN_ERR_ARG;
+  return ATTN_OK;
+}
+
+// Median duration (ms) of `reps` launches of fn on `stream`, after two untimed ones, from HIP
+// events around each launch (synchronises).  Negative on a HIP error (code in *err).
+template <typename F>
+double time_launches(F&& fn, int reps, void* stream, int* err) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<hipEvent_t> ev(2 * size_t(reps), nullptr);
+  double med = -1.0;
+  int e = 0;
+  for (auto& x : ev)
+    if (e == 0) e = int(hipEventCreate(&x));
+  for (int i = 0; i < 2 && e == 0; ++i) e = fn();
+  for (int r = 0; r < reps && e == 0; ++r) {
+    e = int(hipEventRecord(ev[2 * r], s));
+    if (e == 0) e = fn();
+    if (e == 0) e = int(hipEventRecord(ev[2 * r + 1], s));
+  }
+  if (e == 0) e = int(hipEventSynchronize(ev[2 * reps - 1]));
+  if (e == 0) {
+    std::vector<double> t(reps);
+    for (int r = 0; r < reps && e == 0; ++r) {
+      float ms = 0.0f;
+      e = int(hipEventElapsedTime(&ms, ev[2 * r], ev[2 * r + 1]));
+      t[r] = ms;
+    }
+    if (e == 0) {
+      std::sort(t.begin(), t.end());
+      med = t[reps / 2];
+    }
+  }
+  for (auto& x : ev)
+    if (x) (void)hipEventDestroy(x);
+  *err = e;
+  return e == 0 ? med : -1.0;
 }
 
 // The split kernel writing chunk states into the workspace at ws (layout w).
@@ -130,29 +246,14 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, float* o, floa
 attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int H, int Sq, int Sk, int d, float scale, int causal,
                         attn_dtype dtype, attn_dtype out_dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
-  attn_status st = check_shape(B, H, Sq, Sk, d, dtype);
+  float sl2 = 0.0f;
+  attn_status st = check_dense(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, dtype, &sl2);
   if (st != ATTN_OK) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return ATTN_ERR_ALIGN;
-  if ((causal != 0 && causal != 1) || !positive_finite(scale)) return ATTN_ERR_ARG;
-  const float sl2 = static_cast<float>(double(scale) * kLog2e);
-  if (!positive_finite(sl2)) return ATTN_ERR_ARG;
-
   if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
 
-  attn::FwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = static_cast<float*>(o); a.lse = lse;
-  a.o_bf16 = out_dtype == ATTN_BF16;
-  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
-  a.dtype = dtype; a.causal = causal;
-  a.num_splits = 1; a.chunk = Sk; a.split_mode = 0;
-  a.scale_log2 = sl2;
-  a.v_scale = 1.0f;
-  const attn::FwdPlan pl = plan_for(B, H, Sq, d, causal, dtype);
-  a.pair_order = pl.pair_order;
-  a.head_group = pl.head_group;
-  return launched(attn::launch_fwd(a, stream));
+  const attn::FwdPlan pl = plan_for(B, H, Sq, Sk, d, causal, dtype);
+  return launched(launch_dense(q, k, v, o, lse, B, H, Sq, Sk, d, sl2, causal, dtype,
+                               out_dtype == ATTN_BF16, pl, stream));
 }
 
 attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* lse,
@@ -190,6 +291,12 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, float* 
 
 int attn_splitkv_num_splits(int B, int H, int Sq, int Sk, int d, attn_dtype dtype) {
   if (check_shape(B, H, Sq, Sk, d, dtype) != ATTN_OK) return 0;
+  if (g_tuned.load(std::memory_order_acquire) > 0) {
+    const PlanKey key = plan_key(B, H, Sq, Sk, d, -1, dtype);
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    auto it = g_split_counts.find(key);
+    if (it != g_split_counts.end()) return it->second;
+  }
   return attn::splitkv_count(B, H, Sq, Sk, attn::device_cu_count());
 }
 
@@ -308,12 +415,13 @@ const char* attn_bwd_kernel_name(int d, attn_dtype dtype, int which) {
   return attn::bwd_kernel_name(d, which);
 }
 
-int attn_block_m(int B, int H, int Sq, int d, int causal, attn_dtype dtype, int num_splits) {
-  if (B < 1 || H < 1 || Sq < 1 || !supported_d(d) || !supported_dtype(dtype)) return 0;
+int attn_block_m(int B, int H, int Sq, int Sk, int d, int causal, attn_dtype dtype,
+                 int num_splits) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || !supported_d(d) || !supported_dtype(dtype)) return 0;
   if (causal != 0 && causal != 1) return 0;
   if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return 0;
   if (num_splits >= 1) return attn::kBlockM;
-  return plan_for(B, H, Sq, d, causal, dtype).block_m;
+  return plan_for(B, H, Sq, Sk, d, causal, dtype).block_m;
 }
 
 int attn_block_n(int d, attn_dtype dtype) {
@@ -321,19 +429,127 @@ int attn_block_n(int d, attn_dtype dtype) {
   return attn::block_n(dtype, d);
 }
 
-int64_t attn_num_workgroups(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
+int64_t attn_num_workgroups(int B, int H, int Sq, int Sk, int d, int causal, attn_dtype dtype,
                             int num_splits) {
-  const int bm = attn_block_m(B, H, Sq, d, causal, dtype, num_splits);
+  const int bm = attn_block_m(B, H, Sq, Sk, d, causal, dtype, num_splits);
   if (bm == 0) return -1;
   return int64_t(B) * H * ceil_div(Sq, bm) * (num_splits >= 1 ? num_splits : 1);
 }
 
-const char* attn_kernel_name(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
+const char* attn_kernel_name(int B, int H, int Sq, int Sk, int d, int causal, attn_dtype dtype,
                              int num_splits) {
-  if (attn_block_m(B, H, Sq, d, causal, dtype, num_splits) == 0) return "unsupported";
+  if (attn_block_m(B, H, Sq, Sk, d, causal, dtype, num_splits) == 0) return "unsupported";
   if (num_splits >= 1)
     return attn::fwd_kernel_name(dtype, d, 1, splitkv_schedule(B, H, Sq, d, dtype, num_splits));
-  return attn::fwd_kernel_name(dtype, d, 0, plan_for(B, H, Sq, d, causal, dtype).pair_order);
+  return attn::fwd_kernel_name(dtype, d, 0, plan_for(B, H, Sq, Sk, d, causal, dtype).pair_order);
+}
+
+// ---------------------------------------------------------------- shape-keyed tuning
+attn_status attn_tune(const void* q, const void* k, const void* v, float* o, float* lse,
+                      int B, int H, int Sq, int Sk, int d, float scale, int causal,
+                      attn_dtype dtype, int reps, int* plan, void* stream) {
+  float sl2 = 0.0f;
+  attn_status st = check_dense(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, dtype, &sl2);
+  if (st != ATTN_OK) return st;
+  if (reps < 1 || reps > 1000) return ATTN_ERR_ARG;
+  const int cus = attn::device_cu_count();
+  int cand[attn::kMaxPlan];
+  const int n = attn::tune_candidates(B, H, Sq, d, causal, dtype, cus, cand, attn::kMaxPlan);
+  std::vector<double> med(n);
+  for (int i = 0; i < n; ++i) {
+    const attn::FwdPlan pl = plan_of_id(cand[i], B, H, Sq);
+    int err = 0;
+    med[i] = time_launches([&] { return launch_dense(q, k, v, o, lse, B, H, Sq, Sk, d, sl2, causal,
+                                                     dtype, false, pl, stream); },
+                           reps, stream, &err);
+    if (err != 0) return launched(err);
+  }
+  const int best = cand[attn::choose_plan(med.data(), n, attn::kTuneMargin)];
+  {
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    g_plans[plan_key(B, H, Sq, Sk, d, causal, dtype)] = best;
+    g_tuned.store(int(g_plans.size() + g_split_counts.size()), std::memory_order_release);
+  }
+  if (plan) *plan = best;
+  // leave the chosen plan's result in o and lse
+  st = launched(launch_dense(q, k, v, o, lse, B, H, Sq, Sk, d, sl2, causal, dtype, false,
+                             plan_of_id(best, B, H, Sq), stream));
+  if (st != ATTN_OK) return st;
+  return launched(int(hipStreamSynchronize(static_cast<hipStream_t>(stream))));
+}
+
+attn_status attn_tune_splitkv(const void* q, const void* k, const void* v, float* o, float* lse,
+                              int B, int H, int Sq, int Sk, int d, float scale, int causal,
+                              attn_dtype dtype, float q_descale, float k_descale,
+                              float v_descale, int reps, int* num_splits, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  float sl2 = 0.0f;
+  attn_status st = check_splitkv(q, k, v, 1, B, H, Sq, Sk, d, scale, causal, dtype, q_descale,
+                                 k_descale, v_descale, &sl2);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
+  if (reps < 1 || reps > 1000) return ATTN_ERR_ARG;
+  const int64_t rows = int64_t(B) * H * Sq;
+  // candidates: the rule's count first, then 1, 2, 4, ... 64 (chunks of at least one key,
+  // states within the static array, grid indices in range)
+  const int def = attn::splitkv_count(B, H, Sq, Sk, attn::device_cu_count());
+  std::vector<int> cand{def};
+  for (int c = 1; c <= attn::kMaxAutoSplits; c *= 2)
+    if (c != def && c <= Sk && check_shape(B, H, Sq, Sk, d, dtype, c) == ATTN_OK &&
+        attn::workspace_layout(rows, d, c).total <= attn::kNoallocScratchBytes)
+      cand.push_back(c);
+  if (attn::workspace_layout(rows, d, def).total > attn::kNoallocScratchBytes) return ATTN_ERR_WORKSPACE;
+  int err = 0;
+  void* ws = attn::noalloc_scratch(&err);
+  if (ws == nullptr) return launched(err != 0 ? err : 1);
+  std::vector<double> med(cand.size());
+  for (size_t i = 0; i < cand.size(); ++i) {
+    const int c = cand[i];
+    const attn::WorkspaceLayout w = attn::workspace_layout(rows, d, c);
+    med[i] = time_launches([&] {
+      const int e = launch_splitkv(q, k, v, ws, w, c, B, H, Sq, Sk, d, sl2, causal, dtype,
+                                   v_descale, stream);
+      return e != 0 ? e : launch_merge_ws(ws, w, c, o, lse, rows, d, stream);
+    }, reps, stream, &err);
+    if (err != 0) return launched(err);
+  }
+  const int best = cand[attn::choose_plan(med.data(), int(cand.size()), attn::kTuneMargin)];
+  {
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    g_split_counts[plan_key(B, H, Sq, Sk, d, -1, dtype)] = best;
+    g_tuned.store(int(g_plans.size() + g_split_counts.size()), std::memory_order_release);
+  }
+  if (num_splits) *num_splits = best;
+  const attn::WorkspaceLayout w = attn::workspace_layout(rows, d, best);
+  st = launched(launch_splitkv(q, k, v, ws, w, best, B, H, Sq, Sk, d, sl2, causal, dtype, v_descale,
+                               stream));
+  if (st == ATTN_OK) st = launched(launch_merge_ws(ws, w, best, o, lse, rows, d, stream));
+  if (st != ATTN_OK) return st;
+  return launched(int(hipStreamSynchronize(static_cast<hipStream_t>(stream))));
+}
+
+int attn_plan_get(int B, int H, int Sq, int Sk, int d, int causal, attn_dtype dtype) {
+  if (check_shape(B, H, Sq, Sk, d, dtype) != ATTN_OK || (causal != 0 && causal != 1)) return -1;
+  return plan_id_for(B, H, Sq, Sk, d, causal, dtype);
+}
+
+attn_status attn_plan_set(int B, int H, int Sq, int Sk, int d, int causal, attn_dtype dtype,
+                          int plan) {
+  attn_status st = check_shape(B, H, Sq, Sk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
+  if (!attn::plan_legal(plan, int64_t(B) * H, d, causal, dtype)) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  g_plans[plan_key(B, H, Sq, Sk, d, causal, dtype)] = plan;
+  g_tuned.store(int(g_plans.size() + g_split_counts.size()), std::memory_order_release);
+  return ATTN_OK;
+}
+
+void attn_plan_clear(void) {
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  g_plans.clear();
+  g_split_counts.clear();
+  g_tuned.store(0, std::memory_order_release);
 }
 
 const char* attn_status_string(attn_status s) {

@@ -123,6 +123,73 @@ inline int splitkv_count(int B, int H, int Sq, int Sk, int cus) {
   return n;
 }
 
+// ---- shape-keyed tuning ("Inside FlashAttention-3", 7.1 Kernel Tuning: time the candidate
+// configurations on first use and keep the best; "AI 大模型之 FlashAttention_02", 3.3: the
+// best block configuration differs by shape, and the choice must stay reproducible).
+//
+// A launch plan of attn_fwd is the schedule (pair_order 0-3 above) and, for the schedules
+// that use it (0 and 3), the head group; it is exchanged as one integer,
+//     plan = schedule + 4 * log2(head_group),  head_group a power of two <= 64.
+constexpr int kMaxPlan = 4 * 7;
+inline int encode_plan(int sched, int head_group) {
+  int lg = 0;
+  while ((1 << lg) < head_group) ++lg;
+  return sched + 4 * lg;
+}
+inline int plan_sched(int plan) { return plan & 3; }
+inline int plan_head_group(int plan) { return 1 << (plan >> 2); }
+
+// Whether `plan` is a launch plan the kernels implement for this call: the schedule exists
+// for (dtype, d, causal) and the head group divides B*H (schedules 1 and 2 ignore it and
+// take 1).
+inline bool plan_legal(int plan, long long bh, int d, int causal, int dtype) {
+  if (plan < 0 || plan >= kMaxPlan) return false;
+  const int s = plan_sched(plan), g = plan_head_group(plan);
+  if (bh % g != 0) return false;
+  switch (s) {
+    case 0: return true;
+    case 1: return causal == 1 && g == 1;
+    case 2: return causal == 1 && g == 1 && pairs_supported(dtype, d);
+    case 3: return dual_supported(dtype, d);
+  }
+  return false;
+}
+
+// The plan of the fixed rule (plan_fwd), as a plan id.
+inline int default_plan(int B, int H, int Sq, int d, int causal, int dtype, int cus) {
+  const FwdPlan pl = plan_fwd(B, H, Sq, d, causal, dtype, cus);
+  const bool uses_group = pl.pair_order == 0 || pl.pair_order == 3;
+  return encode_plan(pl.pair_order, uses_group ? pl.head_group : 1);
+}
+
+// Candidates timed by attn_tune, default first: every legal schedule, with head groups
+// 1, 2, 4, ... (dividing B*H, up to 64) for the schedules that use one.  Returns the count.
+inline int tune_candidates(int B, int H, int Sq, int d, int causal, int dtype, int cus,
+                           int* out, int cap) {
+  const long long bh = (long long)B * H;
+  int n = 0;
+  const int def = default_plan(B, H, Sq, d, causal, dtype, cus);
+  if (n < cap) out[n++] = def;
+  for (int s = 0; s < 4; ++s)
+    for (int lg = 0; lg < 7; ++lg) {
+      const int p = s + 4 * lg;
+      if (p != def && plan_legal(p, bh, d, causal, dtype) && n < cap) out[n++] = p;
+    }
+  return n;
+}
+
+// The pick from measured median times (same order as the candidates, candidate 0 = the
+// default): the fastest, unless it beats the default by less than `margin` (relative), in
+// which case the default stays; equal times go to the earlier candidate.  Deterministic for
+// given times; the margin keeps run-to-run noise from flipping the choice.
+inline int choose_plan(const double* med, int n, double margin) {
+  int best = 0;
+  for (int i = 1; i < n; ++i)
+    if (med[i] < med[best]) best = i;
+  return (best != 0 && med[best] < (1.0 - margin) * med[0]) ? best : 0;
+}
+constexpr double kTuneMargin = 0.02;
+
 struct MergeArgs {
   const float* ws_m;
   const float* ws_l;

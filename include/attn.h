@@ -282,24 +282,91 @@ const char* attn_bwd_kernel_name(int d, attn_dtype dtype, int which);
  * attn_fwd_splitkv with that many chunks.  A call launches one four-wavefront workgroup
  * per 128 query rows (times num_splits), except causal bf16 calls with d <= 128 whose
  * tile pairs fit one workgroup per CU: those launch one eight-wavefront workgroup per
- * pair of 128-row tiles (t, last - t), 256 query rows.  Causal plans depend on the
- * current device's CU count (a HIP query).
+ * pair of 128-row tiles (t, last - t), 256 query rows.  Plans depend on the current
+ * device's CU count (a HIP query) and on a plan stored for the shape by attn_tune or
+ * attn_plan_set, if any.
  */
 /* Query rows per workgroup, or 0 if an argument is out of range. */
-int attn_block_m(int B, int H, int Sq, int d, int causal, attn_dtype dtype, int num_splits);
+int attn_block_m(int B, int H, int Sq, int Sk, int d, int causal, attn_dtype dtype,
+                 int num_splits);
 
 /* Keys per tile of the key sweep of the four-wavefront kernel for (d, dtype), or 0. */
 int attn_block_n(int d, attn_dtype dtype);
 
 /* Workgroups of the launch: B * H * ceil(Sq / block_m) * max(1, num_splits), or -1. */
-int64_t attn_num_workgroups(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
+int64_t attn_num_workgroups(int B, int H, int Sq, int Sk, int d, int causal, attn_dtype dtype,
                             int num_splits);
 
-/* Name of the kernel instance the call launches (static string; "unsupported" if none):
- * the real kernel name a measurement records with its software versions ("AI 大模型之
- * FlashAttention_02", section "Experiment code and timing discipline"). */
-const char* attn_kernel_name(int B, int H, int Sq, int d, int causal, attn_dtype dtype,
+/* Name of the kernel instance the call launches under the plan in effect (static string;
+ * "unsupported" if none): the real kernel name a measurement records with its software
+ * versions ("AI 大模型之 FlashAttention_02", section "Experiment code and timing
+ * discipline").  The head group of a plan (attn_plan_get) does not change the instance. */
+const char* attn_kernel_name(int B, int H, int Sq, int Sk, int d, int causal, attn_dtype dtype,
                              int num_splits);
+
+/*
+ * Shape-keyed tuning ("Inside FlashAttention-3", section 7.1 Kernel Tuning: benchmark the
+ * candidate configurations once and keep the best for later calls; "AI 大模型之
+ * FlashAttention_02", section 3.3: the best block configuration differs from shape to
+ * shape, and the choice must stay reproducible).
+ *
+ * A launch plan of attn_fwd / attn_fwd_ex is an integer
+ *     plan = schedule + 4 * log2(head_group)
+ * schedule 0: one workgroup per 128-row query tile (causal: longest sweeps first);
+ *          1: (causal) workgroups i and i + grid/2 get complementary query tiles;
+ *          2: (causal bf16, d <= 128) one workgroup per pair of tiles (t, last - t);
+ *          3: (bf16 d <= 128, fp8 d = 128) two wavefront groups per workgroup splitting each
+ *             tile's keys;
+ * head_group (1..64, dividing B*H; schedules 0 and 3 only, else 1): heads whose query tiles
+ * are scheduled together on one XCD.  Every plan computes the same attention; schedules
+ * differ in rounding order only (3 and 2 merge two partial states).  Without a stored plan
+ * a fixed rule picks one (attn_plan_get reports it).
+ *
+ * Plans are kept per process, keyed by (device, its CU count, dtype, d, causal, B, H, Sq,
+ * Sk); stored split counts by the same key without causal.  The table is thread-safe; an
+ * empty table costs attn_fwd nothing.
+ */
+
+/*
+ * attn_tune -- SYNCHRONOUS: times every legal plan of attn_fwd for this shape (`reps`
+ * launches each on `stream`, after two untimed ones; median of HIP-event durations),
+ * stores the winner for the shape, writes its id to *plan (if plan is not NULL), leaves the
+ * winner's O and lse in o / lse and waits for `stream`.  Arguments as for attn_fwd, plus
+ * reps in [1, 1000].  The winner is the fastest median, unless it beats the rule's plan by
+ * less than 2 %, in which case the rule's plan stays (deterministic for given timings; the
+ * margin keeps timing noise from flipping the choice between runs).  Call it before the
+ * timed or captured region, never inside a graph capture.
+ */
+attn_status attn_tune(const void* q, const void* k, const void* v, float* o, float* lse,
+                      int B, int H, int Sq, int Sk, int d, float scale, int causal,
+                      attn_dtype dtype, int reps, int* plan, void* stream);
+
+/*
+ * attn_tune_splitkv -- SYNCHRONOUS: times attn_fwd_splitkv + attn_merge for the split
+ * counts 1, 2, 4, ..., 64 (and attn_splitkv_num_splits' rule), with the chunk states in the
+ * static array of attn_fwd_splitkv_noalloc, stores the winner (same rule as attn_tune), which
+ * attn_splitkv_num_splits returns from then on for (B, H, Sq, Sk, d, dtype), writes it to
+ * *num_splits (if not NULL) and leaves its O and lse in o / lse.  Counts whose states exceed
+ * ATTN_NOALLOC_SCRATCH_BYTES are not tried (ATTN_ERR_WORKSPACE if the rule's own count does
+ * not fit).  Arguments as for attn_fwd_splitkv_noalloc, plus reps in [1, 1000].
+ */
+attn_status attn_tune_splitkv(const void* q, const void* k, const void* v, float* o, float* lse,
+                              int B, int H, int Sq, int Sk, int d, float scale, int causal,
+                              attn_dtype dtype, float q_descale, float k_descale,
+                              float v_descale, int reps, int* num_splits, void* stream);
+
+/* The plan attn_fwd uses for this shape: the stored one, else the rule's; -1 if an argument
+ * is out of range.  With attn_plan_set, a plan chosen in one run can be reused in another. */
+int attn_plan_get(int B, int H, int Sq, int Sk, int d, int causal, attn_dtype dtype);
+
+/* Stores `plan` for the shape on the current device (ATTN_ERR_UNSUPPORTED if it is not a
+ * legal plan of that shape: unknown schedule for dtype / d / causal, head group not dividing
+ * B*H). */
+attn_status attn_plan_set(int B, int H, int Sq, int Sk, int d, int causal, attn_dtype dtype,
+                          int plan);
+
+/* Forgets every stored plan and split count. */
+void attn_plan_clear(void);
 
 /* Human-readable text of a status code (static string). */
 const char* attn_status_string(attn_status s);

@@ -40,7 +40,7 @@ def test_bf16_output_is_the_rounded_fp32_output(dtype, B, H, Sq, Sk, d, causal):
     sc = scale_for(d)
     eff = float(np.float32(sc * sq * sk)) if dtype == "fp8" else sc
     print(f"bf16 out {dtype} B={B} H={H} Sq={Sq} Sk={Sk} d={d} causal={causal} "
-          f"kernel={ea.attn_kernel_name(B, H, Sq, d, int(causal), ea.dtype_code(q))}", flush=True)
+          f"kernel={ea.attn_kernel_name(B, H, Sq, Sk, d, int(causal), ea.dtype_code(q))}", flush=True)
     o32, l32 = ea.attn_fwd(q, k, v, scale=eff, causal=causal)
     o16, l16 = ea.attn_fwd_ex(q, k, v, scale=eff, causal=causal, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()

@@ -272,9 +272,9 @@ def test_causal_tile_pairs_plan_and_parity():
     middle tile pairs with itself), Sq != Sk, ragged last tile."""
     B, H, Sq, Sk, d = 1, 3, 1100, 1500, 128
     nqt = -(-Sq // 128)
-    assert ea.attn_kernel_name(B, H, Sq, d, 1, ea.ATTN_BF16).startswith("attn_fwd_causal_pairs_bf16_d128")
-    assert ea.attn_block_m(B, H, Sq, d, 1, ea.ATTN_BF16) == 256
-    assert ea.attn_num_workgroups(B, H, Sq, d, 1, ea.ATTN_BF16) == B * H * ((nqt + 1) // 2)
+    assert ea.attn_kernel_name(B, H, Sq, Sk, d, 1, ea.ATTN_BF16).startswith("attn_fwd_causal_pairs_bf16_d128")
+    assert ea.attn_block_m(B, H, Sq, Sk, d, 1, ea.ATTN_BF16) == 256
+    assert ea.attn_num_workgroups(B, H, Sq, Sk, d, 1, ea.ATTN_BF16) == B * H * ((nqt + 1) // 2)
     inp = si.make_attention_inputs(B, H, Sq, Sk, d, seed=21, dtype="bf16", hot_row_frac=0.01)
     sc = scale_for(d)
     o, lse = _run_fwd(inp, sc, True)
@@ -286,9 +286,9 @@ def test_small_grids_run_two_groups_per_workgroup():
     """Grids of at most one workgroup per CU split each tile's keys between two groups
     (the split-KV chunks too); parity of those kernels is covered by every small-shape
     test above, this pins the choice."""
-    assert ea.attn_kernel_name(1, 2, 300, 128, 0, ea.ATTN_BF16).startswith("attn_fwd_dual_bf16_d128")
-    assert ea.attn_kernel_name(1, 8, 128, 128, 0, ea.ATTN_FP8_E4M3, 16).startswith("attn_fwd_splitkv_dual_fp8_d128")
-    assert ea.attn_kernel_name(1, 8, 8192, 128, 0, ea.ATTN_BF16) == "attn_fwd_bf16_d128_bm128_bn32"
+    assert ea.attn_kernel_name(1, 2, 300, 300, 128, 0, ea.ATTN_BF16).startswith("attn_fwd_dual_bf16_d128")
+    assert ea.attn_kernel_name(1, 8, 128, 32768, 128, 0, ea.ATTN_FP8_E4M3, 16).startswith("attn_fwd_splitkv_dual_fp8_d128")
+    assert ea.attn_kernel_name(1, 8, 8192, 8192, 128, 0, ea.ATTN_BF16) == "attn_fwd_bf16_d128_bm128_bn32"
     inp = si.make_attention_inputs(1, 2, 300, 333, 128, seed=24, dtype="bf16", hot_row_frac=0.02)
     sc = scale_for(128)
     for causal in (False, True):
@@ -302,8 +302,8 @@ def test_causal_schedules_without_pairs():
     once; bf16 with a grid larger than one workgroup per CU: longest sweeps first."""
     for (B, H, S, d, dtype, seed) in ((1, 2, 700, 64, "fp8", 22), (4, 40, 700, 64, "bf16", 23)):
         adt = ea.ATTN_FP8_E4M3 if dtype == "fp8" else ea.ATTN_BF16
-        assert not ea.attn_kernel_name(B, H, S, d, 1, adt).startswith("attn_fwd_causal_pairs")
-        assert ea.attn_num_workgroups(B, H, S, d, 1, adt) == B * H * -(-S // 128)
+        assert not ea.attn_kernel_name(B, H, S, S, d, 1, adt).startswith("attn_fwd_causal_pairs")
+        assert ea.attn_num_workgroups(B, H, S, S, d, 1, adt) == B * H * -(-S // 128)
         inp = si.make_attention_inputs(B, H, S, S, d, seed=seed, dtype=dtype)
         sc = scale_for(d)
         o, lse = _run_fwd(inp, sc, True)

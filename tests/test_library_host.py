@@ -145,26 +145,26 @@ def test_workgroup_count_follows_the_pages_query_tile_grid(lib):
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "cta_counts.json")))
     for dt in (0, 1, 2):
         for d in (64, 128, 256):
-            bm = lib.attn_block_m(1, 8, 8192, d, 0, dt, 0)
+            bm = lib.attn_block_m(1, 8, 8192, 8192, d, 0, dt, 0)
             assert bm == 128
             for row in g["printed"]:
                 if row["tile_q"] == bm:
-                    got = lib.attn_num_workgroups(row["batch"], row["heads"], row["length"], d, 0, dt, 0)
+                    got = lib.attn_num_workgroups(row["batch"], row["heads"], row["length"], row["length"], d, 0, dt, 0)
                     assert got == row["ctas"]
-            assert lib.attn_num_workgroups(8, 32, 2048, d, 0, dt, 0) == 8 * 32 * 2048 // bm
-            assert lib.attn_block_m(1, 8, 128, d, 0, dt, 16) == 128
-            assert lib.attn_num_workgroups(1, 8, 128, d, 0, dt, 16) == 8 * 16
-            assert lib.attn_num_workgroups(1, 8, 8192, d, 0, dt, 1) == 8 * 64
-            assert lib.attn_num_workgroups(1, 16, 1000, d, 0, dt, 0) == 16 * -(-1000 // bm)
-    assert lib.attn_num_workgroups(1, 8, 8192, 96, 0, 1, 0) == -1
-    assert lib.attn_block_m(1, 8, 8192, 128, 2, 1, 0) == 0
+            assert lib.attn_num_workgroups(8, 32, 2048, 2048, d, 0, dt, 0) == 8 * 32 * 2048 // bm
+            assert lib.attn_block_m(1, 8, 128, 32768, d, 0, dt, 16) == 128
+            assert lib.attn_num_workgroups(1, 8, 128, 32768, d, 0, dt, 16) == 8 * 16
+            assert lib.attn_num_workgroups(1, 8, 8192, 8192, d, 0, dt, 1) == 8 * 64
+            assert lib.attn_num_workgroups(1, 16, 1000, 1000, d, 0, dt, 0) == 16 * -(-1000 // bm)
+    assert lib.attn_num_workgroups(1, 8, 8192, 8192, 96, 0, 1, 0) == -1
+    assert lib.attn_block_m(1, 8, 8192, 8192, 128, 2, 1, 0) == 0
 
 
 def test_kernel_names_and_status_strings(lib):
-    assert lib.attn_kernel_name(1, 8, 8192, 128, 0, 1, 0) == b"attn_fwd_bf16_d128_bm128_bn32"
-    assert lib.attn_kernel_name(1, 8, 8192, 256, 0, 1, 0) == b"attn_fwd_bf16_d256_bm128_bn32"
-    assert lib.attn_kernel_name(1, 8, 128, 128, 0, 2, 4).startswith(b"attn_fwd_splitkv_fp8_d128")
-    assert lib.attn_kernel_name(1, 8, 128, 100, 0, 1, 0) == b"unsupported"
+    assert lib.attn_kernel_name(1, 8, 8192, 8192, 128, 0, 1, 0) == b"attn_fwd_bf16_d128_bm128_bn32"
+    assert lib.attn_kernel_name(1, 8, 8192, 8192, 256, 0, 1, 0) == b"attn_fwd_bf16_d256_bm128_bn32"
+    assert lib.attn_kernel_name(1, 8, 128, 32768, 128, 0, 2, 4).startswith(b"attn_fwd_splitkv_fp8_d128")
+    assert lib.attn_kernel_name(1, 8, 128, 128, 100, 0, 1, 0) == b"unsupported"
     for s in range(8):
         assert lib.attn_status_string(s)
     assert lib.attn_last_hip_error() == 0
@@ -244,3 +244,50 @@ def test_grid_index_bound_follows_the_launch(lib):
     # 16-byte workspace instead)
     assert split(256) == 2
     assert split(128) == 5
+
+
+def test_plan_table_is_keyed_by_the_whole_shape(lib):
+    """attn_plan_set / attn_plan_get / attn_plan_clear on the CPU (no launch): a stored plan
+    applies to exactly its shape; illegal plans are refused; clearing restores the rule."""
+    lib.attn_plan_clear()
+    base = lib.attn_plan_get(1, 4, 1000, 1000, 128, 1, 1)
+    assert base >= 0
+    neighbours = ((1, 4, 1000, 1001, 128, 1, 1), (1, 4, 1001, 1000, 128, 1, 1),
+                  (2, 4, 1000, 1000, 128, 1, 1), (1, 4, 1000, 1000, 64, 1, 1),
+                  (1, 4, 1000, 1000, 128, 0, 1), (1, 4, 1000, 1000, 128, 1, 2))
+    rule = [lib.attn_plan_get(*a) for a in neighbours]
+    other = 4 if base != 4 else 0   # plain schedule, head group 2 (or 1)
+    assert lib.attn_plan_set(1, 4, 1000, 1000, 128, 1, 1, other) == 0
+    assert lib.attn_plan_get(1, 4, 1000, 1000, 128, 1, 1) == other
+    # any other key component (Sk, Sq, B, d, causal, dtype) still gets the rule's plan
+    assert [lib.attn_plan_get(*a) for a in neighbours] == rule
+    # the kernel name follows the stored plan's schedule
+    assert lib.attn_plan_set(1, 4, 1000, 1000, 128, 1, 1, 2) == 0
+    assert lib.attn_kernel_name(1, 4, 1000, 1000, 128, 1, 1, 0).startswith(b"attn_fwd_causal_pairs")
+    assert lib.attn_block_m(1, 4, 1000, 1000, 128, 1, 1, 0) == 256
+    assert lib.attn_plan_set(1, 4, 1000, 1000, 128, 1, 1, 3) == 0
+    assert lib.attn_kernel_name(1, 4, 1000, 1000, 128, 1, 1, 0).startswith(b"attn_fwd_dual")
+    assert lib.attn_plan_set(1, 4, 1000, 1000, 128, 1, 1, 8 + 0) == 0   # plain, head group 4
+    assert lib.attn_plan_get(1, 4, 1000, 1000, 128, 1, 1) == 8
+    # refused: pairs without causal, head group 8 not dividing B*H = 4, out of range, bad shape
+    assert lib.attn_plan_set(1, 4, 1000, 1000, 128, 0, 1, 2) == 4
+    assert lib.attn_plan_set(1, 4, 1000, 1000, 128, 1, 1, 12) == 4
+    assert lib.attn_plan_set(1, 4, 1000, 1000, 128, 1, 1, 99) == 4
+    assert lib.attn_plan_set(0, 4, 1000, 1000, 128, 1, 1, 0) == 2
+    assert lib.attn_plan_get(1, 4, 1000, 1000, 128, 2, 1) == -1
+    lib.attn_plan_clear()
+    assert lib.attn_plan_get(1, 4, 1000, 1000, 128, 1, 1) == base
+
+
+def test_tune_calls_refuse_bad_arguments_before_any_launch(lib):
+    import ctypes
+    out = ctypes.c_int(-7)
+    assert lib.attn_tune(Q, K, V, O, L, 1, 2, 64, 64, 64, 0.125, 0, 1, 0, ctypes.byref(out), None) == 7
+    assert lib.attn_tune(Q, K, V, O, L, 1, 2, 64, 64, 64, 0.125, 0, 1, 1001, ctypes.byref(out), None) == 7
+    assert lib.attn_tune(None, K, V, O, L, 1, 2, 64, 64, 64, 0.125, 0, 1, 5, ctypes.byref(out), None) == 1
+    assert lib.attn_tune(Q, K, V, O, L, 1, 2, 64, 64, 96, 0.125, 0, 1, 5, ctypes.byref(out), None) == 4
+    assert lib.attn_tune_splitkv(Q, K, V, O, L, 1, 2, 64, 64, 64, 0.125, 0, 1, 1.0, 1.0, 1.0, 0,
+                                 ctypes.byref(out), None) == 7
+    assert lib.attn_tune_splitkv(Q, K, V, None, L, 1, 2, 64, 64, 64, 0.125, 0, 1, 1.0, 1.0, 1.0, 5,
+                                 ctypes.byref(out), None) == 1
+    assert out.value == -7

@@ -104,3 +104,57 @@ def test_split_count_follows_the_shape(split_probe):
         (1, 8, 128, 32768, 304),   # more CUs, same shape: still a power of two within the CUs
     ])
     assert out == [32, 1, 1, 4, 2, 64, 1, 32]
+
+
+@pytest.fixture(scope="module")
+def tune_probe(tmp_path_factory):
+    cxx = host_cxx()
+    exe = str(tmp_path_factory.mktemp("tune") / "tune_probe")
+    subprocess.run([cxx, "-std=c++17", "-O1", os.path.join(HERE, "tune_probe.cpp"), "-o", exe], check=True)
+
+    def run(lines):
+        out = subprocess.run([exe], input="".join(l + "\n" for l in lines), capture_output=True,
+                             text=True, check=True).stdout
+        return out.strip().splitlines()
+    return run
+
+
+def test_tuning_candidates_are_the_legal_plans_default_first(tune_probe):
+    # causal bf16 d=128, B=1, H=4, S=1000 on 256 CUs: the rule picks tile pairs (plan 2);
+    # schedules 0 and 3 come with head groups 1, 2, 4 (dividing B*H = 4), 1 alone
+    out = tune_probe(["cand 1 4 1000 128 1 1 256"])
+    cand = [int(x) for x in out[0].split()]
+    assert cand[0] == 2
+    assert sorted(cand) == sorted([0, 4, 8, 1, 2, 3, 7, 11])
+    # non-causal fp32: no dual, pair or complementary schedule; B*H = 6 allows head groups 1, 2
+    cand = [int(x) for x in tune_probe(["cand 2 3 512 64 0 0 256"])[0].split()]
+    assert sorted(cand) == [0, 4]
+
+
+def test_plan_legality(tune_probe):
+    cases = [
+        ("legal 2 8 128 1 1", 1),    # tile pairs: causal bf16 d=128
+        ("legal 2 8 256 1 1", 0),    # not for d=256
+        ("legal 2 8 128 0 1", 0),    # not without the causal mask
+        ("legal 1 8 64 1 2", 1),     # complementary tiles: any causal call
+        ("legal 5 8 64 1 2", 0),     # ... which ignores head groups
+        ("legal 3 8 128 0 2", 1),    # two groups: fp8 d=128
+        ("legal 3 8 64 0 2", 0),     # but not fp8 d=64
+        ("legal 3 8 64 0 0", 0),     # nor fp32
+        ("legal 12 8 128 0 1", 1),   # plain with head group 8 dividing B*H = 8
+        ("legal 16 8 128 0 1", 0),   # head group 16 does not divide 8
+        ("legal 28 64 128 0 1", 0),  # out of range
+        ("legal -1 8 128 0 1", 0),
+    ]
+    assert [int(x) for x in tune_probe([c for c, _ in cases])] == [r for _, r in cases]
+
+
+def test_plan_choice_is_deterministic_with_a_margin_for_the_default(tune_probe):
+    out = tune_probe([
+        "choose 3 100 99 98.5",     # best beats the default by 1.5 %: the default stays
+        "choose 3 100 97 97.5",     # 3 % faster: candidate 1
+        "choose 3 100 97 97",       # equal times: the earlier candidate
+        "choose 1 42",              # a single candidate
+        "choose 4 100 110 90 90",   # ties after the default: the first of them
+    ] * 2)                           # and the same answers when asked again
+    assert out == ["0", "1", "1", "0", "2"] * 2
