@@ -22,6 +22,8 @@ Prints one JSON line.  Besides the headline throughput it carries
                 fraction also against the peak at that clock;
   environment   GPU name / arch / CUs, ROCm, hipcc and torch versions, CPU model, host
                 cores, NumPy and its BLAS.
+Before the warm-up, attn_tune picks and stores the launch plan of each mask for the
+workload's shape (--no-tune: the fixed rule); config.plans records them.
 With the CPU leg, a few sampled rows of two heads are also checked against the oracle's
 outputs (outside the timed region).
 
@@ -624,6 +626,8 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="use the fixed launch-plan rule instead of attn_tune's choice")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--sweep", choices=("c1", "c2", "c4", "c5", "bwd", "varlen", "out16"),
@@ -691,6 +695,16 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # shape-keyed tuning (synchronous, before the warm-up and the timed region): the plans
+    # attn_tune keeps for this shape are the ones the timed calls use
+    plans = {}
+    for c in modes:
+        name = "causal" if c else "non_causal"
+        plan = (ea.attn_tune(q, k, v, scale=scale, causal=c, reps=10, out=o, lse=lse)
+                if not args.no_tune else ea.attn_plan_get(B, H, S, S, d, c, ea.ATTN_BF16))
+        sched, group = ea.plan_parts(plan)
+        plans[name] = {"plan": plan, "schedule": sched, "head_group": group, "tuned": not args.no_tune}
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -744,6 +758,7 @@ def main():
                         "fp32 O + lse; one step = non-causal + causal forward",
             "B": B, "H": H, "Sq": S, "Sk": S, "d": d, "masks": ["non-causal", "causal"],
             "kernels": {m: ea.attn_kernel_name(B, H, S, S, d, c, ea.ATTN_BF16) for m, c in (("non_causal", 0), ("causal", 1))},
+            "plans": plans,
         },
         "modes": {
             ("causal" if c else "non_causal"): {
