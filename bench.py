@@ -156,16 +156,25 @@ def summarize_traffic(fetch_dir: str, write_dir: str, probe_mib: int, workload: 
     ])
 
 
+def _kernel_key(r) -> str:
+    """Short name of an attention kernel instance plus its workgroup count (one kernel
+    instance serves several grid sizes, e.g. split counts)."""
+    k = r["Kernel_Name"].replace("void attn::(anonymous namespace)::", "").split("(attn::")[0]
+    grid = int(float(r.get("Grid_Size") or r.get("Grid_Size_X") or 0))
+    wg = int(float(r.get("Workgroup_Size") or r.get("Workgroup_Size_X") or 0))
+    return f"{k} [{grid // wg} wg]" if grid and wg else k
+
+
 def summarize_pmc(dirs) -> str:
     """Markdown table of `rocprofv3 --pmc` counter runs (one directory per pass): the mean
-    per dispatch of every counter, for each attention kernel instance seen."""
+    per dispatch of every counter, for each attention kernel instance and grid seen."""
     acc = {}
     for d in dirs:
         per = {}
         for r in _csv_rows(d, "_counter_collection.csv"):
             if "attn_" not in r["Kernel_Name"]:
                 continue
-            key = (r["Kernel_Name"], r["Counter_Name"], r["Dispatch_Id"])
+            key = (_kernel_key(r), r["Counter_Name"], r["Dispatch_Id"])
             per[key] = per.get(key, 0.0) + float(r["Counter_Value"])  # sum over instances
         for (k, c, _), v in per.items():
             acc.setdefault((k, c), []).append(v)
@@ -173,14 +182,13 @@ def summarize_pmc(dirs) -> str:
     for d in dirs:
         for r in _csv_rows(d, "_kernel_trace.csv"):
             if "attn_" in r["Kernel_Name"]:
-                dur.setdefault(r["Kernel_Name"], []).append(
+                dur.setdefault(_kernel_key(r), []).append(
                     (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3)
-    short = lambda k: k.replace("void attn::(anonymous namespace)::", "").split("(attn::")[0]
     out = ["| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
     for k, us in sorted(dur.items()):
-        out.append(f"| {short(k)} | duration (us, counter runs) | {len(us)} | {np.mean(us):.1f} |")
+        out.append(f"| {k} | duration (us, counter runs) | {len(us)} | {np.mean(us):.1f} |")
     for (k, c), vs in sorted(acc.items()):
-        out.append(f"| {short(k)} | {c} | {len(vs)} | {np.mean(vs):.6g} |")
+        out.append(f"| {k} | {c} | {len(vs)} | {np.mean(vs):.6g} |")
     return "\n".join(out)
 
 

@@ -26,7 +26,10 @@
 // only when a new score exceeds it by more than kTau (log2 units), which bounds the
 // unnormalised probabilities by 2^kTau and leaves the exact result unchanged (the
 // final division uses the same reference), while skipping most rescales of the
-// output accumulator.
+// output accumulator.  The bf16 and fp8 main loops skip even the tile's row maximum:
+// they take the probabilities against the reference as it stands and redo the tile
+// against its maximum only when the probabilities' sum shows the reference was too
+// low for the format (bf16: a lane sum past 2^32; fp8: a probability past E4M3's 448).
 //
 // Split mode computes, for one chunk of the keys, the unnormalised state (m, l, u) of
 // the split-K section of "AI 大模型之 FlashAttention_02" and stores it in a
@@ -96,13 +99,18 @@ template <> struct Traits<DT_FP8> {
   using POp = long;
   static constexpr int kBytes = 1, kKPL = 32, kKS = 64;
   static constexpr bool kDMA = true;
-  // FP8 probabilities are scaled by 2^8 before rounding to E4M3 (max 448) so that
-  // they sit in the format's normal range.  The reference may lag the row maximum by
-  // kTau = 0.75 (log2 units): probabilities stay <= 2^0.75 = 1.68, i.e. <= 431 after the
-  // 2^8 scale, inside E4M3's range, and the accumulator is rescaled only when a maximum
-  // moves by more than that.
-  static constexpr float kTau = 0.75f;
-  static constexpr float kPScale = 256.0f;
+  // FP8 probabilities are scaled by 2^kPExp before rounding to E4M3 (max 448) so that
+  // most of them sit in the format's normal range.  The reference may lag the row
+  // maximum by kTau (log2 units), so probabilities reach 2^(kPExp + kTau) and the two
+  // must stay below log2(448) = 8.807.  The split is a trade: kPExp = 4, kTau = 4.75
+  // keeps probabilities down to 2^-10 normal (2^-13 as subnormals, absolute error at
+  // most 2^-14 against row sums >= 1) and rescales the accumulator only when a row
+  // maximum moves by more than 4.75, which after the first tile of a chunk is rare;
+  // kTau = 0.75 with kPExp = 8 rescaled on most tiles of short chunks.
+  static constexpr int kPExp = 4;
+  static constexpr float kTau = 4.75f;
+  static constexpr float kPScale = float(1 << kPExp);
+  static_assert(kPExp + kTau < 8.807f, "scaled probabilities must stay below E4M3's 448");
   __device__ static f32x16_t mfma(Op a, Op b, f32x16_t c) {
     // formats 0 / 0: E4M3 for both operands; scales 127 = 2^0
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
@@ -562,12 +570,36 @@ __device__ __forceinline__ float softmax_rescale(const f32x16_t (&s)[BN / 32], f
   return (m_run == -__builtin_inff()) ? 0.0f : m_run;
 }
 
+// Probabilities (already scaled by 2^kPExp) -> E4M3 value-MFMA operands.  Each 32-bit
+// word takes two conversions (low half, then high half); written as one asm pair with
+// an output-only word, so that no register has to be cleared or copied for the half the
+// first conversion leaves alone.
+__device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d) {
+  uint32_t w;
+  asm("v_cvt_pk_fp8_f32 %0, %1, %2\n\tv_cvt_pk_fp8_f32 %0, %3, %4 op_sel:[0,0,1]"
+      : "=&v"(w) : "v"(a), "v"(b), "v"(c), "v"(d));
+  return w;
+}
+template <int BN>
+__device__ __forceinline__ void pack_fp8(const f32x16_t (&p)[BN / 32], PTile<DT_FP8, BN>& pt) {
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 8 * h;
+      const uint32_t lo = cvt4_fp8(p[b][e + 0], p[b][e + 1], p[b][e + 2], p[b][e + 3]);
+      const uint32_t hi = cvt4_fp8(p[b][e + 4], p[b][e + 5], p[b][e + 6], p[b][e + 7]);
+      pt.pk[b][h] = (long)(((unsigned long)hi << 32) | lo);
+    }
+}
+
 template <int DT, int BN>
 __device__ __forceinline__ void softmax_exp(f32x16_t (&s)[BN / 32], PTile<DT, BN>& pt, float ms,
                                             float sl2) {
   using TR = Traits<DT>;
-  // FP8 probabilities come out scaled by kPScale = 2^8 (an exponent offset of 8).
-  const float mo = DT == DT_FP8 ? ms - 8.0f : ms;
+  // FP8 probabilities come out scaled by kPScale (an exponent offset of kPExp).
+  float mo = ms;
+  if constexpr (DT == DT_FP8) mo = ms - float(TR::kPExp);
 #pragma unroll
   for (int b = 0; b < BN / 32; ++b)
 #pragma unroll
@@ -582,20 +614,7 @@ __device__ __forceinline__ void softmax_exp(f32x16_t (&s)[BN / 32], PTile<DT, BN
         pt.pk[b][h] = __builtin_convertvector(x, bf16x8_t);
       }
   } else if constexpr (DT == DT_FP8) {
-    static_assert(TR::kPScale == 256.0f, "exponent offset above assumes 2^8");
-#pragma unroll
-    for (int b = 0; b < BN / 32; ++b)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int w[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int e = 8 * h + 4 * q;
-          int v = __builtin_amdgcn_cvt_pk_fp8_f32(s[b][e + 0], s[b][e + 1], 0, false);
-          w[q] = __builtin_amdgcn_cvt_pk_fp8_f32(s[b][e + 2], s[b][e + 3], v, true);
-        }
-        pt.pk[b][h] = (long)(((unsigned long)(uint32_t)w[1] << 32) | (uint32_t)w[0]);
-      }
+    pack_fp8<BN>(s, pt);
   }
 }
 
@@ -624,7 +643,7 @@ __device__ __forceinline__ void softmax_sums(const f32x16_t (&s)[BN / 32], const
         }
     c_run += cs;
   } else if constexpr (DT == DT_FP8) {
-    // the packed sum comes from fp8_psum (an MFMA), folded into c_run by the sweep
+    // the packed sum comes from fp8_psum (an MFMA), read into c_run after the sweep
   } else {
     c_run += ls;
   }
@@ -654,10 +673,11 @@ __device__ __forceinline__ float softmax_exp_ref(const f32x16_t (&s)[BN / 32], f
   return ls;
 }
 
+// (eoff: exponent offset of the probabilities, kPExp for fp8, 0 otherwise)
 template <int BN, int NDB>
 __device__ __forceinline__ float softmax_redo(const f32x16_t (&s)[BN / 32], f32x16_t (&p)[BN / 32],
                                               f32x16_t (&oacc)[NDB], float& m_run, float& l_run,
-                                              float& c_run, float sl2) {
+                                              float& c_run, float sl2, float eoff = 0.0f) {
   float mx = -__builtin_inff();
 #pragma unroll
   for (int b = 0; b < BN / 32; ++b)
@@ -672,18 +692,21 @@ __device__ __forceinline__ float softmax_redo(const f32x16_t (&s)[BN / 32], f32x
     for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
     m_run = m_new;
   }
-  return softmax_exp_ref<BN>(s, p, m_run == -__builtin_inff() ? 0.0f : m_run, sl2);
+  return softmax_exp_ref<BN>(s, p, (m_run == -__builtin_inff() ? 0.0f : m_run) - eoff, sl2);
 }
 
 // FP8: the column sums of a tile's packed probabilities (one per query, the same in every
 // accumulator element of the lane) from one 64-deep MFMA with an all-ones E4M3 block
 // (0x38 = 1.0) as the A operand: exact products, fp32 accumulation like the value MFMA.
-__device__ __forceinline__ f32x16_t fp8_psum(const PTile<DT_FP8, 64>& pt) {
+// The sums accumulate in an accumulator block of their own, next to the value blocks,
+// which every rescale of the accumulator scales with them; nothing reads it before the
+// end of the sweep, so no step waits on this MFMA.
+__device__ __forceinline__ void fp8_psum(const PTile<DT_FP8, 64>& pt, f32x16_t& acc) {
   const i32x8_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};
   const i32x8_t pb = __builtin_bit_cast(i32x8_t, (long __attribute__((ext_vector_type(4)))){
       pt.pk[0][0], pt.pk[0][1], pt.pk[1][0], pt.pk[1][1]});
-  return Traits<DT_FP8>::mfma(ones, pb, f32x16_t{});
+  acc = Traits<DT_FP8>::mfma(ones, pb, acc);
 }
 
 // Probabilities -> value-MFMA operands (bf16), and the sum of exactly those values.
@@ -854,6 +877,9 @@ __device__ __forceinline__ void interleave_deferred() {
   sched_pairs<NM, 0x8, 1, 0x2, (NV + NM - 1) / NM>();
 }
 
+// Largest finite E4M3 value.
+constexpr float kFp8Max = 448.0f;
+
 // ================================================================== forward kernel
 // MODE kPlain: O and lse of one 128-row query tile per workgroup (four wavefronts).
 // MODE kSplit: the unnormalised state of one key chunk of one query tile.
@@ -994,8 +1020,21 @@ void attn_fwd_kernel(FwdArgs p) {
   // ---- per-wavefront state of the query tile being swept
   int q0 = 0, r0 = 0, row = 0, wave_last = 0;
   Op qop[KSTEPS];
-  f32x16_t oacc[NDB];
+  // O^T blocks, and for fp8 one more block that accumulates the packed sums
+  constexpr int NACC = NDB + (DT == DT_FP8 ? 1 : 0);
+  f32x16_t oacc[NACC];
   float m_run, l_run, c_run;  // reference maximum (log2 units), row sum, consistent row sum
+  auto ov = [&]() __attribute__((always_inline)) -> f32x16_t(&)[NDB] {
+    return *reinterpret_cast<f32x16_t(*)[NDB]>(&oacc[0]);
+  };
+  // FP8: c_run from the packed-sum block (every lane holds its query's full sum; half
+  // of it goes to each of the two lanes whose partial sums pair_sum adds)
+  auto take_csum = [&]() __attribute__((always_inline)) {
+    if constexpr (DT == DT_FP8) c_run = oacc[NDB][0] * (0.5f / TR::kPScale);
+  };
+  auto add_psum = [&](const PTile<DT, BN>& pt) __attribute__((always_inline)) {
+    if constexpr (DT == DT_FP8) fp8_psum(pt, oacc[NDB]);
+  };
   const float sl2 = p.scale_log2;
 
   // Start query tile `tile`: its rows, its Q operands (B operand of S^T = K Q^T, in
@@ -1019,7 +1058,7 @@ void attn_fwd_kernel(FwdArgs p) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) oacc[i] = f32x16_t{};
+    for (int i = 0; i < NACC; ++i) oacc[i] = f32x16_t{};
     m_run = -__builtin_inff();  // same in lanes c and c+32
     l_run = 0.0f;               // this lane's share of the row sum
     c_run = 0.0f;               // same, of the probabilities as rounded for the MFMA
@@ -1106,7 +1145,7 @@ void attn_fwd_kernel(FwdArgs p) {
       // tile 0's softmax (registers only) while key tile 2 and value tile 0 land
       if (act0) {
         if (needs_mask(kbeg)) mask_tile<BN>(sa, kbeg, kend, row, off, p.causal, g);
-        softmax_tile<DT, BN, NDB>(sa, pa, oacc, m_run, l_run, c_run, sl2);
+        softmax_tile<DT, BN, NACC>(sa, pa, oacc, m_run, l_run, c_run, sl2);
       }
       P::template wait_loads<2>();  // key tile 2 and value tile 0
       block_sync();
@@ -1137,7 +1176,7 @@ void attn_fwd_kernel(FwdArgs p) {
         // (cs is in the test only so that the packing stays ahead of the branch; it is
         // close to ls and non-finite exactly when ls is)
         if (__builtin_amdgcn_ballot_w64(!(ls + cs <= 2.0f * kSumCap))) {
-          ls = softmax_redo<BN, NDB>(s_cur, pr, oacc, m_run, l_run, c_run, sl2);
+          ls = softmax_redo<BN, NACC>(s_cur, pr, oacc, m_run, l_run, c_run, sl2);
           cs = pack_bf16<BN>(pr, pnext);
         }
         l_run += ls;
@@ -1156,10 +1195,10 @@ void attn_fwd_kernel(FwdArgs p) {
         pipe.issue_k(rk, k0 + 5 * BN, kdst);
         pipe.issue_v(rv, k0 + 3 * BN, vdst);
         if (act_2) pipe.qk(s_next, kb, qop);
-        if (act_t) pipe.pv(oacc, s_cur, pcur, vb);
+        if (act_t) pipe.pv(ov(), s_cur, pcur, vb);
         if (act_1) {
           if (needs_mask(k0 + BN)) mask_tile<BN>(s_cur, k0 + BN, kend, row, off, p.causal, g);
-          softmax_tile<DT, BN, NDB>(s_cur, pnext, oacc, m_run, l_run, c_run, sl2);
+          softmax_tile<DT, BN, NACC>(s_cur, pnext, oacc, m_run, l_run, c_run, sl2);
         }
         finish_d();
       };
@@ -1229,21 +1268,6 @@ void attn_fwd_kernel(FwdArgs p) {
     // O^T += V^T P^T with tile t's values.  Key tile t+NS and value tile t+NS-1 are
     // requested into the stages that iteration t-1 finished reading; at the end of
     // the iteration only the loads that iteration t+1 needs are waited for.
-    // FP8: each active tile's packed-probability sum is computed by fp8_psum after its
-    // value MFMAs and folded into c_run at the next step, before that step's possible
-    // rescale (c_run and the sum share the reference of the tile), so nothing waits on
-    // the MFMA.  Every lane holds its query's full sum; half of it goes to each of the
-    // two lanes whose partial sums pair_sum adds.
-    [[maybe_unused]] f32x16_t psum = {};
-    auto fold_psum = [&]() __attribute__((always_inline)) {
-      if constexpr (DT == DT_FP8) {
-        c_run += psum[0] * (0.5f / TR::kPScale);
-        psum[0] = 0.0f;
-      }
-    };
-    auto take_psum = [&](const PTile<DT, BN>& pt) __attribute__((always_inline)) {
-      if constexpr (DT == DT_FP8) psum = fp8_psum(pt);
-    };
     auto finish = [&](uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
       pipe.commit_k(kdst, gtid);
       pipe.commit_v(vdst, gtid);
@@ -1274,17 +1298,33 @@ void attn_fwd_kernel(FwdArgs p) {
         float ls = softmax_exp_ref<BN>(s_cur, pr, m_run, sl2);
         interleave_exp<D, BN>();
         if (__builtin_amdgcn_ballot_w64(!(ls <= kSumCap)))
-          ls = softmax_redo<BN, NDB>(s_cur, pr, oacc, m_run, l_run, c_run, sl2);
+          ls = softmax_redo<BN, NACC>(s_cur, pr, oacc, m_run, l_run, c_run, sl2);
         l_run += ls;
         c_run += pack_bf16<BN>(pr, pt);
         pv_regs<DT, D, BN>(oacc, pt, vo);
         interleave_pv<D, BN>();
+      } else if constexpr (DT == DT_FP8 && D <= 128) {
+        // No row maximum: the probabilities are taken against the reference as it
+        // stands, 2^kPExp-scaled.  Their lane sum bounds every one of them, so a sum
+        // <= 448 (E4M3's largest value) means they pack without overflow and the
+        // reference may stay (it then lags the row maximum by at most
+        // log2(448) - kPExp); otherwise -- or with no reference yet -- the tile is
+        // redone against its row maximum.  (d = 256 keeps the row maximum: the
+        // extra probability tile would spill there.)
+        pipe.qk(s_next, kb, qop);
+        f32x16_t pr[NKB];
+        float ls = softmax_exp_ref<BN>(s_cur, pr, m_run - float(TR::kPExp), sl2);
+        if (__builtin_amdgcn_ballot_w64(!(ls <= kFp8Max)))
+          ls = softmax_redo<BN, NACC>(s_cur, pr, oacc, m_run, l_run, c_run, sl2, float(TR::kPExp));
+        l_run += ls * (1.0f / TR::kPScale);
+        pack_fp8<BN>(pr, pt);
+        pipe.pv(ov(), s_cur, pt, vb);
+        add_psum(pt);
       } else {
         pipe.qk(s_next, kb, qop);
-        fold_psum();
-        softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
-        pipe.pv(oacc, s_cur, pt, vb);
-        take_psum(pt);
+        softmax_tile<DT, BN, NACC>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
+        pipe.pv(ov(), s_cur, pt, vb);
+        add_psum(pt);
       }
       finish(kdst, vdst);
     };
@@ -1298,13 +1338,12 @@ void attn_fwd_kernel(FwdArgs p) {
       pipe.issue_k(rk, k0 + NS * BN, kdst);
       pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
       if (act_next) pipe.qk(s_next, kb, qop);
-      fold_psum();
       if (act_cur) {
         if (needs_mask(k0)) mask_tile<BN>(s_cur, k0, kend, row, off, p.causal, g);
         PTile<DT, BN> pt;
-        softmax_tile<DT, BN, NDB>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
-        pipe.pv(oacc, s_cur, pt, vb);
-        take_psum(pt);
+        softmax_tile<DT, BN, NACC>(s_cur, pt, oacc, m_run, l_run, c_run, sl2);
+        pipe.pv(ov(), s_cur, pt, vb);
+        add_psum(pt);
       }
       finish(kdst, vdst);
     };
@@ -1349,11 +1388,11 @@ void attn_fwd_kernel(FwdArgs p) {
     };
     run(std::true_type{}, 0, nfull);
     run(std::false_type{}, nfull, ntiles);
-    fold_psum();  // the last tile's packed sum
     // Drain every load before the rings are reused, by this group or the next sweep.
     wait_vmem();
     block_sync();
     }
+    take_csum();
   };
 
   // ---- write-back: deferred normalisation
