@@ -145,10 +145,11 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, float* 
  *     u [n][B][H][Sq][d] sum over the chunk of exp(S - m) * v * v_descale (not divided by l)
  * A chunk state is defined up to its reference: (m + t, l e^-t, u e^-t) is the same state
  * and merges to the same result.  m is the chunk maximum of the scaled scores or lags it:
- * the kernel moves its reference lazily, so m >= max - lag with lag = 0.75 ln 2 for FP8
- * inputs, 8 ln 2 for fp32 inputs and 33 ln 2 (about 22.9) for bf16 inputs (the bf16 key
- * sweep re-references only when a probability would pass 2^33).  A chunk that fits one
- * key tile stores its exact maximum.  m + ln l (the chunk's log-sum-exp) and u / l (its
+ * the kernel moves its reference lazily, so m >= max - lag with lag = (log2(448) - 4) ln 2
+ * (about 3.33) for FP8 inputs (the 2^4-scaled probabilities stay at or below E4M3's
+ * largest value, 448), 8 ln 2 for fp32 inputs and 33 ln 2 (about 22.9) for bf16 inputs
+ * (the bf16 key sweep re-references only when a probability would pass 2^33).  A chunk
+ * that fits one key tile stores its exact maximum.  m + ln l (the chunk's log-sum-exp) and u / l (its
  * normalised weighted average) do not depend on that choice.  (The split-K section of
  * "AI 大模型之 FlashAttention_02", engineering practice, asks the interface to state this
  * local-statistics layout: axis, per-chunk ownership and merge operator.)
