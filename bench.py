@@ -165,6 +165,39 @@ def _kernel_key(r) -> str:
     return f"{k} [{grid // wg} wg]" if grid and wg else k
 
 
+def summarize_traffic_grid(fetch_dir: str, write_dir: str, probe_mib: int) -> str:
+    """HBM bytes per launch of every attention kernel instance and grid in two `rocprofv3
+    --pmc` runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, summed over instances),
+    each scaled by what the same counter reads for the plain device copy of `probe_mib`
+    MiB that the run's --copy-probe-mib performs."""
+    res = {}
+    factors = {}
+    for name, dd in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per, copies = {}, []
+        for r in _csv_rows(dd, "_counter_collection.csv"):
+            if r["Counter_Name"] != name:
+                continue
+            if "copyBuffer" in r["Kernel_Name"]:
+                copies.append(float(r["Counter_Value"]))
+            elif "attn_" in r["Kernel_Name"]:
+                key = (_kernel_key(r), r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        probe = float(np.median(sorted(copies)[-3:]))
+        factors[name] = (probe, probe_mib * 1024.0 / probe)
+        for (k, _), v in per.items():
+            res.setdefault((k, name), []).append(v)
+    out = [f"copy probe {probe_mib} MiB: FETCH_SIZE {factors['FETCH_SIZE'][0]:.1f} KiB "
+           f"(factor {factors['FETCH_SIZE'][1]:.4f}), WRITE_SIZE {factors['WRITE_SIZE'][0]:.1f} KiB "
+           f"(factor {factors['WRITE_SIZE'][1]:.4f})", "",
+           "| kernel [workgroups] | launches | HBM read MB / launch | HBM write MB / launch |",
+           "|---|---|---|---|"]
+    for k in sorted({k for (k, _) in res}):
+        rd = np.mean(res.get((k, "FETCH_SIZE"), [np.nan])) * factors["FETCH_SIZE"][1] * 1024 / 1e6
+        wr = np.mean(res.get((k, "WRITE_SIZE"), [np.nan])) * factors["WRITE_SIZE"][1] * 1024 / 1e6
+        out.append(f"| {k} | {len(res.get((k, 'FETCH_SIZE'), []))} | {rd:.2f} | {wr:.2f} |")
+    return "\n".join(out)
+
+
 def summarize_pmc(dirs) -> str:
     """Markdown table of `rocprofv3 --pmc` counter runs (one directory per pass): the mean
     per dispatch of every counter, for each attention kernel instance and grid seen."""
@@ -260,7 +293,6 @@ def measure_clock(launch, torch, seconds: float = 2.5):
 def environment(torch, dev) -> dict:
     """Versions and hardware the measurement ran on (recorded beside the numbers)."""
     import platform
-    import subprocess
     env = {}
     try:
         pr = torch.cuda.get_device_properties(dev)
@@ -275,11 +307,17 @@ def environment(torch, dev) -> dict:
         env["rocm"] = open("/opt/rocm/.info/version").read().strip()
     except OSError:
         env["rocm"] = None
+    # the HIP compiler's version from the installed header, not by running hipcc: this
+    # process has initialised the GPU, and its children must not replace themselves
     try:
-        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
-                             timeout=30).stdout
-        env["hipcc"] = next((l.strip() for l in out.splitlines() if "version" in l.lower()), None)
-    except Exception:  # noqa: BLE001
+        hv = {}
+        for line in open("/opt/rocm/include/hip/hip_version.h"):
+            parts = line.split()
+            if len(parts) == 3 and parts[0] == "#define" and parts[1].startswith("HIP_VERSION_"):
+                hv[parts[1]] = parts[2].strip('"')
+        env["hipcc"] = (f"HIP version: {hv['HIP_VERSION_MAJOR']}.{hv['HIP_VERSION_MINOR']}."
+                        f"{hv['HIP_VERSION_PATCH']}-{hv.get('HIP_VERSION_GITHASH', '')}")
+    except (OSError, KeyError):
         env["hipcc"] = None
     cpu = None
     try:
@@ -368,8 +406,12 @@ def _stats(us):
             "p90_us": round(float(np.percentile(us, 90)), 2), "min_us": round(float(us.min()), 2)}
 
 
-def sweep(name: str, reps: int, warmup: int):
-    """Per-case timing of the parity workloads; prints one JSON line per case."""
+def sweep(name: str, reps: int, warmup: int, splits=None, seqs=None, masks=(False, True),
+          copy_probe_mib: int = 0):
+    """Per-case timing of the parity workloads; prints one JSON line per case.  splits
+    (c5), seqs (c4) and masks (c1, c2, c4) restrict the cases; copy_probe_mib runs the
+    plain device copy that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters
+    first."""
     import torch
     import exact_attention_82_amd as ea
     import synthetic_inputs as si
@@ -377,6 +419,13 @@ def sweep(name: str, reps: int, warmup: int):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB
+    if copy_probe_mib:
+        src = torch.ones(copy_probe_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def to_dev(inp):
         if inp.dtype == "bf16":
@@ -394,7 +443,8 @@ def sweep(name: str, reps: int, warmup: int):
             cases = [(8, 32, 2048, 64, 2, "bf16", 0.0)]
         else:
             cases = [(B, 16, S, d, 400 + (d // 64) * 100 + S // 100 + B, "bf16", 0.01)
-                     for d in (64, 128, 256) for S in (512, 1000, 2048) for B in (1, 8)]
+                     for d in (64, 128, 256) for S in (512, 1000, 2048) for B in (1, 8)
+                     if not seqs or S in seqs]
         for (B, H, S, d, seed, dt, hot) in cases:
             inp = si.make_attention_inputs(B, H, S, S, d, seed=seed, dtype=dt, hot_row_frac=hot)
             q, k, v = to_dev(inp)
@@ -403,7 +453,7 @@ def sweep(name: str, reps: int, warmup: int):
             o = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
             lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
             in_bytes = 4 if dt == "f32" else 2
-            for causal in (False, True):
+            for causal in masks:
                 fn = lambda: ea.attn_fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
                 for _ in range(warmup):
                     fn()
@@ -557,7 +607,7 @@ def sweep(name: str, reps: int, warmup: int):
         o = torch.empty((B, H, Sq, d), dtype=torch.float32, device=dev)
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
         auto_n = ea.attn_splitkv_num_splits(B, H, Sq, Sk, d, ea.ATTN_FP8_E4M3)
-        for n in (1, 4, 16, 32, 64):
+        for n in splits or (1, 4, 16, 32, 64):
             ws = torch.empty(ea.attn_splitkv_workspace_bytes(B, H, Sq, d, n), dtype=torch.uint8, device=dev)
             f1 = lambda: ea.attn_fwd_splitkv(q, k, v, n, scale=scale, descales=inp.scales, ws=ws)
             f2 = lambda: ea.attn_merge(ws, n, B, H, Sq, d, out=o, lse=lse)
@@ -641,11 +691,17 @@ def main():
     ap.add_argument("--sweep", choices=("c1", "c2", "c4", "c5", "bwd", "varlen", "out16"),
                     help="per-case timing of a parity workload (JSON lines)")
     ap.add_argument("--sweep-reps", type=int, default=30)
+    ap.add_argument("--splits", default="", help="c5 sweep: comma-separated split counts")
+    ap.add_argument("--seqs", default="", help="c4 sweep: comma-separated sequence lengths")
+    ap.add_argument("--masks", default="both", choices=("both", "full", "causal"),
+                    help="c1/c2/c4 sweeps: which masks to run")
     ap.add_argument("--summarize-sweep", metavar="JSONL")
     ap.add_argument("--summarize-stats", metavar="DIR",
                     help="print a table of a rocprofv3 --stats output directory and exit")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
                     help="print per-kernel means of rocprofv3 --pmc counter runs and exit")
+    ap.add_argument("--summarize-traffic-grid", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print HBM bytes per launch of every attention kernel and grid and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print HBM bytes per launch from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
@@ -658,6 +714,9 @@ def main():
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc))
         return
+    if args.summarize_traffic_grid:
+        print(summarize_traffic_grid(*args.summarize_traffic_grid, probe_mib=args.copy_probe_mib or 512))
+        return
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic, probe_mib=args.copy_probe_mib or 512,
                                 workload=args.workload))
@@ -668,7 +727,10 @@ def main():
         sys.exit(2)
 
     if args.sweep:
-        sweep(args.sweep, args.sweep_reps, args.warmup)
+        ints = lambda t: [int(x) for x in t.split(",") if x.strip()]
+        masks = {"both": (False, True), "full": (False,), "causal": (True,)}[args.masks]
+        sweep(args.sweep, args.sweep_reps, args.warmup, splits=ints(args.splits),
+              seqs=ints(args.seqs), masks=masks, copy_probe_mib=args.copy_probe_mib)
         return
 
     import torch

@@ -1099,6 +1099,12 @@ void attn_fwd_kernel(FwdArgs p) {
   // iterations.  Every group of the workgroup passes the same number of barriers
   // (2 + ntiles): iterations past this group's own keys only keep the barrier cadence.
   auto sweep = [&](int kbeg, int kend, int ntiles) __attribute__((always_inline)) {
+    // The key and value slices end at kend: the ring's loads past the range (the last
+    // iterations' look-ahead) then return zeros without touching memory, instead of
+    // fetching the next keys -- another group's or another chunk's -- for nothing.
+    const uint32_t kv_end = uint32_t(kend) * uint32_t(D * EB);
+    const Slice ksl{rk.base, rk.bytes < kv_end ? rk.bytes : kv_end};
+    const Slice vsl{rv.base, rv.bytes < kv_end ? rv.bytes : kv_end};
     // A tile starting at key k0 has work for this wavefront unless it starts past the
     // range, every row of the wavefront is past Sq, or (causal) every key of the tile
     // is above the wavefront's diagonal.
@@ -1125,12 +1131,12 @@ void attn_fwd_kernel(FwdArgs p) {
       f32x16_t sa[NKB], sb[NKB];
       PTile<DT, BN> pa, pb;
       if (ntiles > 0) {
-        pipe.issue_k(rk, kbeg + 0 * BN, kst(0));
-        pipe.issue_k(rk, kbeg + 1 * BN, kst(1));
-        pipe.issue_k(rk, kbeg + 2 * BN, kst(2));
-        pipe.issue_v(rv, kbeg + 0 * BN, vst(0));
-        pipe.issue_k(rk, kbeg + 3 * BN, kst(3));
-        pipe.issue_v(rv, kbeg + 1 * BN, vst(1));
+        pipe.issue_k(ksl, kbeg + 0 * BN, kst(0));
+        pipe.issue_k(ksl, kbeg + 1 * BN, kst(1));
+        pipe.issue_k(ksl, kbeg + 2 * BN, kst(2));
+        pipe.issue_v(vsl, kbeg + 0 * BN, vst(0));
+        pipe.issue_k(ksl, kbeg + 3 * BN, kst(3));
+        pipe.issue_v(vsl, kbeg + 1 * BN, vst(1));
       }
       P::template wait_loads<2>();  // key tiles 0 and 1
       block_sync();
@@ -1139,8 +1145,8 @@ void attn_fwd_kernel(FwdArgs p) {
       if (ntiles > 1 && active(kbeg + BN)) pipe.qk(sb, kst(1), qop);
       block_sync();  // key tile 0's stage is free again
       if (ntiles > 0) {
-        pipe.issue_k(rk, kbeg + 4 * BN, kst(0));
-        pipe.issue_v(rv, kbeg + 2 * BN, vst(2));
+        pipe.issue_k(ksl, kbeg + 4 * BN, kst(0));
+        pipe.issue_v(vsl, kbeg + 2 * BN, vst(2));
       }
       // tile 0's softmax (registers only) while key tile 2 and value tile 0 land
       if (act0) {
@@ -1161,8 +1167,8 @@ void attn_fwd_kernel(FwdArgs p) {
                            f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB], const PTile<DT, BN>& pcur,
                            PTile<DT, BN>& pnext) __attribute__((always_inline)) {
         const int k0 = kbeg + t * BN;
-        pipe.issue_k(rk, k0 + 5 * BN, kdst);
-        pipe.issue_v(rv, k0 + 3 * BN, vdst);
+        pipe.issue_k(ksl, k0 + 5 * BN, kdst);
+        pipe.issue_v(vsl, k0 + 3 * BN, vdst);
         KOps<DT, D, BN> ko;
         VOps<DT, D, BN> vo;
         load_kops<DT, D, BN>(ko, kb, pipe.ln);
@@ -1192,8 +1198,8 @@ void attn_fwd_kernel(FwdArgs p) {
         const bool act_t = t < ntiles && active(k0);
         const bool act_1 = t + 1 < ntiles && active(k0 + BN);
         const bool act_2 = t + 2 < ntiles && active(k0 + 2 * BN);
-        pipe.issue_k(rk, k0 + 5 * BN, kdst);
-        pipe.issue_v(rv, k0 + 3 * BN, vdst);
+        pipe.issue_k(ksl, k0 + 5 * BN, kdst);
+        pipe.issue_v(vsl, k0 + 3 * BN, vdst);
         if (act_2) pipe.qk(s_next, kb, qop);
         if (act_t) pipe.pv(ov(), s_cur, pcur, vb);
         if (act_1) {
@@ -1248,10 +1254,10 @@ void attn_fwd_kernel(FwdArgs p) {
     if (ntiles > 0) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        pipe.issue_k(rk, kbeg + j * BN, kst(j));
+        pipe.issue_k(ksl, kbeg + j * BN, kst(j));
         pipe.commit_k(kst(j), gtid);
         if (j < NS - 1) {
-          pipe.issue_v(rv, kbeg + j * BN, vst(j));
+          pipe.issue_v(vsl, kbeg + j * BN, vst(j));
           pipe.commit_v(vst(j), gtid);
         }
       }
@@ -1282,8 +1288,8 @@ void attn_fwd_kernel(FwdArgs p) {
     auto step_full = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
                          f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB]) __attribute__((always_inline)) {
       const int k0 = kbeg + t * BN;
-      pipe.issue_k(rk, k0 + NS * BN, kdst);
-      pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
+      pipe.issue_k(ksl, k0 + NS * BN, kdst);
+      pipe.issue_v(vsl, k0 + (NS - 1) * BN, vdst);
       PTile<DT, BN> pt;
       if constexpr (P::kRegOps) {
         // Both operand sets are read first (their LDS latency overlaps the row
@@ -1335,8 +1341,8 @@ void attn_fwd_kernel(FwdArgs p) {
       const int k0 = kbeg + t * BN;
       const bool act_cur = active(k0);
       const bool act_next = t + 1 < ntiles && active(k0 + BN);
-      pipe.issue_k(rk, k0 + NS * BN, kdst);
-      pipe.issue_v(rv, k0 + (NS - 1) * BN, vdst);
+      pipe.issue_k(ksl, k0 + NS * BN, kdst);
+      pipe.issue_v(vsl, k0 + (NS - 1) * BN, vdst);
       if (act_next) pipe.qk(s_next, kb, qop);
       if (act_cur) {
         if (needs_mask(k0)) mask_tile<BN>(s_cur, k0, kend, row, off, p.causal, g);
