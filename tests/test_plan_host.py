@@ -73,10 +73,15 @@ def test_without_a_device_query_plans_are_plain(probe):
 
 
 def test_head_group_divides_heads_and_fits_an_xcd(probe):
-    for bh, nqt in [(256, 16), (8, 64), (6, 3), (7, 5), (12, 4), (1, 1)]:
+    # a group of heads divides B*H, its query tiles fit an XCD's 64 resident workgroups,
+    # and it is at most an eighth of the heads (one XCD's share of the renumbered grid)
+    for bh, nqt in [(256, 16), (8, 64), (6, 3), (7, 5), (12, 4), (1, 1), (16, 4), (128, 4), (64, 1)]:
         (_, _, g), = probe([(1, bh, nqt * 128, 64, 0, BF16, 1)])
-        assert bh % g == 0 and (g == 1 or g * nqt <= 64)
-        assert not (bh % (2 * g) == 0 and 2 * g * nqt <= 64)   # largest such power of two
+        assert bh % g == 0 and (g == 1 or (g * nqt <= 64 and 8 * g <= bh))
+        # largest such power of two
+        assert not (bh % (2 * g) == 0 and 2 * g * nqt <= 64 and 16 * g <= bh)
+    assert probe([(1, 16, 512, 64, 0, BF16, 1)])[0][2] == 2      # was 16: 4 XCDs per head
+    assert probe([(8, 32, 2048, 64, 0, BF16, 1)])[0][2] == 4
 
 
 @pytest.fixture(scope="module")
