@@ -220,6 +220,45 @@ def test_config5_fp8_splitkv(n):
         np.testing.assert_allclose(ug / lg[:, None], su / sl[:, None], atol=5e-2)
 
 
+# fp8 with hot query rows (scaled by 4): their scores pass the running reference by more
+# than the lag allows on tiles in the middle of a sweep, so the main loop's redo
+# (reference moved to the tile's maximum, accumulator and sums rescaled) runs on full
+# tiles, in the direct and the split kernels, one and two groups, with a tail tile.
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_hot_rows_direct_and_split(d, causal):
+    inp = si.make_attention_inputs(1, 4, 300, 2500, d, seed=31 + d, dtype="fp8",
+                                   hot_row_frac=0.05, hot_scale=4.0)
+    sc = scale_for(d)
+    sq, sk, sv = inp.scales
+    ro, rl = oracle.attention(inp.q64, inp.k64, inp.v64, sc, causal)
+    q, k, v = upload(inp)
+    o, lse = ea.attn_fwd(q, k, v, scale=float(np.float32(sc * sq * sk)), causal=causal)
+    check(f"fp8 hot rows d={d} causal={causal} attn_fwd", _np(o) * sv, _np(lse), ro, rl, "fp8")
+    for n in (1, 3, 8):
+        _, o2, l2 = _run_split(inp, sc, causal, n, descales=inp.scales)
+        check(f"fp8 hot rows d={d} causal={causal} split n={n}", o2, l2, ro, rl, "fp8")
+
+
+# Rows scaled by 30 give scores around 100-150: O stays within the fp8 bars, while lse
+# carries the score's accumulation error in the 64-deep E4M3 MFMA, measured at about
+# 1.5e-5 of |lse| (the fp32 path on the same values: 4.5e-5 absolute), so the absolute
+# 1e-3 bar holds only up to |lse| of about 60; this test checks O and that relative bound.
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_large_scores_lse_relative(d):
+    inp = si.make_attention_inputs(1, 4, 300, 2500, d, seed=31 + d, dtype="fp8", hot_row_frac=0.05)
+    sc = scale_for(d)
+    sq, sk, sv = inp.scales
+    ro, rl = oracle.attention(inp.q64, inp.k64, inp.v64, sc, False)
+    q, k, v = upload(inp)
+    o, lse = ea.attn_fwd(q, k, v, scale=float(np.float32(sc * sq * sk)), causal=False)
+    loose = dict(TOL["fp8"], lse=float("inf"))
+    check(f"fp8 large scores d={d}", _np(o) * sv, _np(lse), ro, rl, "fp8", tol=loose)
+    rel = np.abs(_np(lse).astype(np.float64) - rl) / np.maximum(np.abs(rl), 1.0)
+    print(f"fp8 large scores d={d}: max |dlse|/|lse| = {rel.max():.3e}", flush=True)
+    assert rel.max() <= 3e-5
+
+
 def test_config5_fp8_direct_forward_with_folded_descales():
     inp = si.make_attention_inputs(1, 8, 128, 32768, 128, seed=5, dtype="fp8")
     sc = scale_for(128)
