@@ -23,6 +23,10 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     # never emit packed fp32 VALU ops (v_pk_fma_f32 and friends)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs unless the code names the accumulation registers (the d = 256
+    # dK/dV kernel does); the two-wavefront kernels (d <= 128) compile to the same code
+    # either way
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

@@ -1752,6 +1752,53 @@ __device__ __forceinline__ void store_rows(float* out, int r0, int nrows, int c,
     }
 }
 
+// dV^T and dK^T accumulation of the d = 256 dK/dV kernel.  Its two accumulators (8
+// blocks of 16 registers each) fill all 256 accumulation registers, so their MFMAs name
+// that register class (inline asm, "+a"); the library is built with MFMA results in VGPRs
+// by default, so S and dP stay in the 256 VGPRs.  (Left to itself the compiler put S and
+// dP among the accumulators and spilled 154 registers per lane, or, with the accumulators
+// pinned, moved two accumulator blocks out and back every tile.)  The compiler does not
+// see these instructions as MFMAs, so it inserts none of their hazard waits: each one
+// starts with the two wait states a VALU write of its A or B operand needs, and nothing
+// else reads or writes the accumulators between agpr_settle calls -- the zeroing before
+// the sweep and the reads of the write-back each sit behind one, which waits out the
+// MFMA pipeline.  Within the sweep an accumulator block is read again as the MFMA's C
+// operand only 7 MFMAs later.
+__device__ __forceinline__ void mfma_bf16_agpr(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+template <int N>
+__device__ __forceinline__ void agpr_settle(f32x16_t (&x)[N], f32x16_t (&y)[N]) {
+  asm volatile("s_nop 15\n\ts_nop 15" : "+a"(x[0]));  // 32 wait states
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    asm volatile("" : "+a"(x[i]));
+    asm volatile("" : "+a"(y[i]));
+  }
+}
+// pv_dma (bf16) with the accumulation in mfma_bf16_agpr.
+template <int D>
+__device__ __forceinline__ void pv_dma_agpr(f32x16_t (&oacc)[D / 32], const PTile<DT_BF16, 32>& pt,
+                                            const uint8_t* vt, const DmaLane<DT_BF16, D, 32>& ln) {
+  using G = DmaGeo<DT_BF16, D, 32>;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bf16x8_t pb = pt.pk[0][h];
+    const int roff = h * 16 * G::ROWB;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int dx = db << 6;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(vt + roff + (ln.vx[0] ^ dx)));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(vt + roff + (ln.vx[1] ^ dx)));
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
+      const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      mfma_bf16_agpr(oacc[db], __builtin_bit_cast(bf16x8_t, both), pb);
+    }
+  }
+}
+
 // Row-operand offset into a tile stored in the value layout: lane (c, g) reads 16-byte
 // chunk 2*ks + g of row c as `tile + (x ^ (ks << 5))`, the same access the key layout
 // gives with DmaLane::kx, so one copy of a tile serves both its row reads and its
@@ -1842,6 +1889,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     dkt[i] = f32x16_t{};
     dvt[i] = f32x16_t{};
   }
+  constexpr bool kAgpr = D >= 256;  // accumulators pinned to the accumulation registers
+  if constexpr (kAgpr) agpr_settle(dkt, dvt);
   Pipe<DT_BF16, D, 32, kWaves> pipe(wave, lane);  // direct-to-LDS tile loads
   const DmaLane<DT_BF16, D, 32>& ln = pipe.ln;
   const int xv = row_lane_offset_vlayout<D>(lane);
@@ -1890,8 +1939,13 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     PTile<DT_BF16, 32> pp, ps;
     pack_tile(pv, pp);
     pack_tile(sv, ps);
-    pv_dma<DT_BF16, D, 32>(dvt, pp, os, ln);  // dV^T += dO^T P
-    pv_dma<DT_BF16, D, 32>(dkt, ps, qs, ln);  // dK^T += Q^T dS
+    if constexpr (kAgpr) {
+      pv_dma_agpr<D>(dvt, pp, os, ln);
+      pv_dma_agpr<D>(dkt, ps, qs, ln);
+    } else {
+      pv_dma<DT_BF16, D, 32>(dvt, pp, os, ln);  // dV^T += dO^T P
+      pv_dma<DT_BF16, D, 32>(dkt, ps, qs, ln);  // dK^T += Q^T dS
+    }
   };
 
 #pragma unroll
@@ -1913,6 +1967,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       block_sync();
     }
   }
+  if constexpr (kAgpr) agpr_settle(dkt, dvt);
   if (part == 1) {  // second half: to the workspace, added by attn_bwd_combine_kernel
     const size_t po = size_t(bh) * size_t(L) * kBlockM;
     store_rows<D>(a.pdk + po * D, kw0, a.Sk, c, g, dkt, a.scale);
