@@ -1776,6 +1776,12 @@ __device__ __forceinline__ void agpr_settle(f32x16_t (&x)[N], f32x16_t (&y)[N]) 
     asm volatile("" : "+a"(y[i]));
   }
 }
+template <int N>
+__device__ __forceinline__ void agpr_settle1(f32x16_t (&x)[N]) {
+  asm volatile("s_nop 15\n\ts_nop 15" : "+a"(x[0]));  // 32 wait states
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(x[i]));
+}
 // pv_dma (bf16) with the accumulation in mfma_bf16_agpr.
 template <int D>
 __device__ __forceinline__ void pv_dma_agpr(f32x16_t (&oacc)[D / 32], const PTile<DT_BF16, 32>& pt,
@@ -2038,6 +2044,8 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   f32x16_t dqt[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqt[i] = f32x16_t{};
+  constexpr bool kAgpr = D >= 256;  // accumulators pinned to the accumulation registers
+  if constexpr (kAgpr) agpr_settle1(dqt);
   Pipe<DT_BF16, D, 32, kWaves> pipe(wave, lane);  // direct-to-LDS tile loads
   const DmaLane<DT_BF16, D, 32>& ln = pipe.ln;
 
@@ -2082,7 +2090,8 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     }
     PTile<DT_BF16, 32> ps;
     pack_tile(sv, ps);
-    pv_dma<DT_BF16, D, 32>(dqt, ps, kv, ln);  // dQ^T += K^T dS^T
+    if constexpr (kAgpr) pv_dma_agpr<D>(dqt, ps, kv, ln);  // dQ^T += K^T dS^T
+    else pv_dma<DT_BF16, D, 32>(dqt, ps, kv, ln);
   };
 
   if (ntiles > 0) issue(0, kv0, vk0);
@@ -2103,6 +2112,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
       }
     }
   }
+  if constexpr (kAgpr) agpr_settle1(dqt);
   store_rows<D>(a.dq + qo * D, r0, a.Sq, c, g, dqt, a.scale);
 }
 
