@@ -1511,8 +1511,9 @@ void attn_fwd_kernel(FwdArgs p) {
     }
     }
     // A hands its state of the shared tile to B through LDS (the rings are drained): the
-    // accumulator block db of lane L of wavefront w goes to ks<db>[(w * 64 + L) * 16],
-    // the running maximum and sums to vs0.
+    // 16-byte piece jj of accumulator block db of lane L of wavefront w goes to
+    // ks<db>[(jj * 256 + w * 64 + L) * 4] -- consecutive lanes write consecutive 16 bytes,
+    // free of bank conflicts -- the running maximum and sums to vs0.
     static_assert(NDB <= NS, "one ring stage array per accumulator block");
     static_assert(P::STAGE_K * NG >= kWaves * 64 * 16 * 4, "stage array holds a block");
     float* hand_m = reinterpret_cast<float*>(vs0);
@@ -1520,12 +1521,12 @@ void attn_fwd_kernel(FwdArgs p) {
     if (grp == 0) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        float* dst = reinterpret_cast<float*>(db == 0 ? ks0 : db == 1 ? ks1 : db == 2 ? ks2 : ks3) + slot * 16;
+        float* dst = reinterpret_cast<float*>(db == 0 ? ks0 : db == 1 ? ks1 : db == 2 ? ks2 : ks3) + slot * 4;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           f32x4_t v4 = {oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2],
                         oacc[db][4 * jj + 3]};
-          *reinterpret_cast<f32x4_t*>(dst + 4 * jj) = v4;
+          *reinterpret_cast<f32x4_t*>(dst + jj * (kWaves * 64 * 4)) = v4;
         }
       }
       hand_m[slot * 3 + 0] = m_run;
@@ -1542,10 +1543,10 @@ void attn_fwd_kernel(FwdArgs p) {
       const float wb = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const float* src = reinterpret_cast<const float*>(db == 0 ? ks0 : db == 1 ? ks1 : db == 2 ? ks2 : ks3) + slot * 16;
+        const float* src = reinterpret_cast<const float*>(db == 0 ? ks0 : db == 1 ? ks1 : db == 2 ? ks2 : ks3) + slot * 4;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(src + 4 * jj);
+          const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(src + jj * (kWaves * 64 * 4));
 #pragma unroll
           for (int e = 0; e < 4; ++e) oacc[db][4 * jj + e] = wa * v4[e] + wb * oacc[db][4 * jj + e];
         }
