@@ -186,6 +186,19 @@ def test_backward_is_deterministic_and_leaves_inputs_alone():
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_d256_long_sweeps(causal):
+    """d = 256 at S = 1024 (32 query tiles per key sweep, 8 key tiles per query sweep): the
+    dK/dV and dQ accumulators of these kernels run through many MFMA chains per call."""
+    B, H, S, d = 1, 2, 1024, 256
+    inp, do = _inputs(B, H, S, S, d, seed=77 + int(causal))
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    o, lse = _oracle_fwd(inp, scale, causal)
+    q, k, v = upload(inp)
+    got = _run_bwd(q, k, v, o, lse, do, scale, causal)
+    _check_heads(inp, do, scale, causal, got, label=f"bwd 1x2x1024 d=256 causal={causal}")
+
+
 def test_backward_one_head_at_training_size():
     """B=1, H=4, S=2048, d=128, causal: head 3 compared in full (the others must be finite)."""
     B, H, S, d = 1, 4, 2048, 128
