@@ -167,12 +167,18 @@ __device__ __forceinline__ void block_sync() {
 // 16 consecutive rows at the same column; the key swizzle gives those rows distinct
 // banks.  Value tile (bf16): the transposed LDS read (ds_read_b64_tr_b16) has each
 // 16-lane group fetch 4 consecutive rows x 32 bytes; the value swizzle puts the 4 rows
-// of a group, and the two groups sharing a cycle, on distinct banks.
+// of a group, and the two groups sharing a cycle, on distinct banks.  Value tile
+// (fp8): the transposed read (ds_read_b64_tr_b8) has each 32-lane half fetch rows
+// {0..3, 8..11} (+4 in the upper half) x two adjacent 16-byte chunks; the value swizzle
+// gives the rows that share a bank row (same row mod 256/ROWB) distinct chunk pairs.
 template <int ROWB> __device__ __forceinline__ int swz_k(int r) {
   return ROWB >= 256 ? (r & 15) : ROWB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 template <int DT, int ROWB> __device__ __forceinline__ int swz_v(int r) {
-  if constexpr (DT == DT_FP8) return swz_k<ROWB>(r);
+  if constexpr (DT == DT_FP8)
+    return ROWB >= 256 ? (((r & 3) | ((r >> 1) & 4)) << 1)
+         : ROWB == 128 ? ((((r >> 1) & 1) | ((r >> 2) & 2)) << 1)
+                       : ((r >> 2) & 3);
   return ROWB >= 256 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
@@ -257,7 +263,7 @@ template <int DT, int D, int BN> struct DmaLane {
       kx2 = c * G::ROWB + (((2 * g + 1) ^ f) << 4);
       const int s = (lane & 15) >> 1, hi = (lane >> 4) & 1;
       const int keyin = s < 4 ? g * 4 + s : 8 + g * 4 + (s - 4);
-      const int fv = swz_k<G::ROWB>(keyin);
+      const int fv = swz_v<DT, G::ROWB>(keyin);
       vx[0] = keyin * G::ROWB + ((hi ^ fv) << 4) + ((lane & 1) << 3);
       vx[1] = 0;
     }
