@@ -1349,6 +1349,24 @@ void attn_fwd_kernel(FwdArgs p) {
       const bool act_next = t + 1 < ntiles && active(k0 + BN);
       pipe.issue_k(ksl, k0 + NS * BN, kdst);
       pipe.issue_v(vsl, k0 + (NS - 1) * BN, vdst);
+      if constexpr (P::kRegOps) {
+        // bf16: the main loop's lazy softmax (no row maximum unless the reference has
+        // to move), with the mask where the tile needs one
+        if (act_next) pipe.qk(s_next, kb, qop);
+        if (act_cur) {
+          if (needs_mask(k0)) mask_tile<BN>(s_cur, k0, kend, row, off, p.causal, g);
+          PTile<DT, BN> pt;
+          f32x16_t pr[NKB];
+          float ls = softmax_exp_ref<BN>(s_cur, pr, m_run, sl2);
+          if (__builtin_amdgcn_ballot_w64(!(ls <= kSumCap)))
+            ls = softmax_redo<BN, NACC>(s_cur, pr, oacc, m_run, l_run, c_run, sl2);
+          l_run += ls;
+          c_run += pack_bf16<BN>(pr, pt);
+          pipe.pv(ov(), s_cur, pt, vb);
+        }
+        finish(kdst, vdst);
+        return;
+      }
       if (act_next) pipe.qk(s_next, kb, qop);
       if (act_cur) {
         if (needs_mask(k0)) mask_tile<BN>(s_cur, k0, kend, row, off, p.causal, g);
