@@ -398,6 +398,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o
   a.lse2 = reinterpret_cast<float*>(base + w.lse2_off);
   a.pdk = reinterpret_cast<float*>(base + w.pdk_off);
   a.pdv = reinterpret_cast<float*>(base + w.pdv_off);
+  a.pdq = reinterpret_cast<float*>(base + w.pdq_off);
   a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
   a.causal = causal;
   a.scale = scale;
@@ -407,6 +408,9 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o
   const int64_t nkt = (Sk + attn::kBlockM - 1) / attn::kBlockM;
   const int cus = attn::device_cu_count();
   a.long_tiles = (cus > 0 && bh * nkt <= 2 * int64_t(cus)) ? attn::bwd_long_tiles(Sq, Sk, causal) : 0;
+  // the same for the dQ grid and its long query tiles
+  const int64_t nqt = (Sq + attn::kBlockM - 1) / attn::kBlockM;
+  a.long_qtiles = (cus > 0 && bh * nqt <= 2 * int64_t(cus)) ? attn::bwd_long_qtiles(Sq, Sk, causal) : 0;
   return launched(attn::launch_bwd(a, stream));
 }
 

@@ -242,6 +242,8 @@ struct BwdArgs {
   int long_tiles;    // key tiles 0..long_tiles-1 are swept in two halves (causal, small grids)
   float* pdk;        // workspace [B*H][long_tiles*128][d]: second halves' dK
   float* pdv;        // same for dV
+  int long_qtiles;   // the last long_qtiles query tiles' dQ sweeps go in two halves (same)
+  float* pdq;        // workspace [B*H][long_qtiles*128][d]: second halves' dQ
 };
 
 // Query tiles (of 32 rows) the dK/dV sweep of 128-key tile kt visits: rows from
@@ -263,8 +265,32 @@ inline int bwd_long_tiles(int Sq, int Sk, int causal) {
   return n;
 }
 
+// Key tiles (of 32) the dQ sweep of 128-row query tile qt visits: up to the tile's last
+// row's diagonal (causal).
+inline int bwd_key_tiles(int Sq, int Sk, int qt, int causal) {
+  int kend = Sk;
+  if (causal) {
+    const int last = ((qt + 1) * 128 < Sq ? (qt + 1) * 128 : Sq) - 1;
+    kend = last + (Sk - Sq) + 1;
+    kend = kend < 0 ? 0 : kend > Sk ? Sk : kend;
+  }
+  return (kend + 31) / 32;
+}
+
+// Causal query tiles whose dQ sweep covers more than half of the longest one (a suffix:
+// the sweeps grow with qt), swept in two halves under the same condition as the long key
+// tiles.
+inline int bwd_long_qtiles(int Sq, int Sk, int causal) {
+  if (!causal) return 0;
+  const int nqt = (Sq + 127) / 128;
+  const int longest = bwd_key_tiles(Sq, Sk, nqt - 1, 1);
+  int n = 0;
+  while (n < nqt && bwd_key_tiles(Sq, Sk, nqt - 1 - n, 1) > (longest + 1) / 2) ++n;
+  return n;
+}
+
 struct BwdWorkspaceLayout {
-  size_t do_off, dsum_off, lse2_off, pdk_off, pdv_off, total;
+  size_t do_off, dsum_off, lse2_off, pdk_off, pdv_off, pdq_off, total;
 };
 
 inline BwdWorkspaceLayout bwd_workspace_layout(int64_t bh, int Sq, int Sk, int d, int causal) {
@@ -272,13 +298,15 @@ inline BwdWorkspaceLayout bwd_workspace_layout(int64_t bh, int Sq, int Sk, int d
   const size_t rows = size_t(bh) * size_t(Sq);
   const int lt = bwd_long_tiles(Sq, Sk, causal);
   const size_t prow = size_t(bh) * size_t(lt) * 128;
+  const size_t qrow = size_t(bh) * size_t(bwd_long_qtiles(Sq, Sk, causal)) * 128;
   BwdWorkspaceLayout w;
   w.do_off = 0;
   w.dsum_off = up(rows * size_t(d) * 2);
   w.lse2_off = w.dsum_off + up(rows * sizeof(float));
   w.pdk_off = w.lse2_off + up(rows * sizeof(float));
   w.pdv_off = w.pdk_off + up(prow * size_t(d) * sizeof(float));
-  w.total = w.pdv_off + up(prow * size_t(d) * sizeof(float));
+  w.pdq_off = w.pdv_off + up(prow * size_t(d) * sizeof(float));
+  w.total = w.pdq_off + up(qrow * size_t(d) * sizeof(float));
   return w;
 }
 

@@ -2009,8 +2009,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
-// dK, dV of the split key tiles: first half (already in place) + second half (workspace),
-// in that order, so the sum does not depend on timing.
+// dK, dV of the split key tiles and dQ of the split query tiles: first half (already in
+// place) + second half (workspace), in that order, so the sum does not depend on timing.
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void attn_bwd_combine_kernel(BwdArgs a) {
@@ -2023,6 +2023,17 @@ void attn_bwd_combine_kernel(BwdArgs a) {
     const size_t w = size_t(bh * int64_t(a.long_tiles) * kBlockM + kr) * D + col;
     *reinterpret_cast<f32x4_t*>(a.dk + o) += *reinterpret_cast<const f32x4_t*>(a.pdk + w);
     *reinterpret_cast<f32x4_t*>(a.dv + o) += *reinterpret_cast<const f32x4_t*>(a.pdv + w);
+  }
+  // the long query tiles are the last ones: rows [q_first, Sq) of every (batch, head)
+  const int q_first = (ceil_div_i(a.Sq, kBlockM) - a.long_qtiles) * kBlockM;
+  const int qrows = a.Sq - q_first;
+  const int64_t m4 = a.long_qtiles > 0 ? int64_t(a.B) * a.H * qrows * (D / 4) : 0;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < m4; i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / (D / 4), col = (i % (D / 4)) * 4;
+    const int64_t bh = r / qrows, qr = r % qrows;
+    const size_t o = size_t(bh * a.Sq + q_first + qr) * D + col;
+    const size_t w = size_t(bh * int64_t(a.long_qtiles) * kBlockM + qr) * D + col;
+    *reinterpret_cast<f32x4_t*>(a.dq + o) += *reinterpret_cast<const f32x4_t*>(a.pdq + w);
   }
 }
 
@@ -2041,8 +2052,19 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const int BH = a.B * a.H;
   const int nqt = ceil_div_i(a.Sq, kBlockM);
   const int bh = blockIdx.x % BH;
-  int qt = blockIdx.x / BH;
-  if (a.causal) {  // longest (last) query tiles first, paired with short ones per CU
+  const int item = blockIdx.x / BH;
+  const int LQ = a.long_qtiles;
+  int qt = item, part = -1;  // part -1: the whole sweep; 0 / 1: its first / second half
+  if (LQ > 0) {
+    // Longest items first: the two halves of each long (last) query tile, then the other
+    // tiles from the longest down.
+    if (item < 2 * LQ) {
+      qt = nqt - 1 - item / 2;
+      part = item % 2;
+    } else {
+      qt = nqt - 1 - LQ - (item - 2 * LQ);
+    }
+  } else if (a.causal) {  // longest (last) query tiles first, paired with short ones per CU
     const int half = (nqt + 1) / 2;
     qt = qt < half ? nqt - 1 - qt : qt - half;
   }
@@ -2087,7 +2109,10 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     const int last_row = min((qt + 1) * kBlockM, a.Sq) - 1;
     kend = max(0, min(a.Sk, last_row + off + 1));
   }
-  const int ntiles = ceil_div_i(kend, 32);
+  // this item's key tiles [kt0, kt0 + ntiles)
+  const int nall = ceil_div_i(kend, 32);
+  const int kt0 = part == 1 ? nall / 2 : 0;
+  const int ntiles = part == 0 ? nall / 2 : nall - kt0;
 
   auto kvst = [&](int j) __attribute__((always_inline)) -> uint8_t* {
     return j % 3 == 0 ? kv0 : j % 3 == 1 ? kv1 : kv2;
@@ -2119,8 +2144,9 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     else pv_dma<DT_BF16, D, 32>(dqt, ps, kv, ln);
   };
 
-  if (ntiles > 0) issue(0, kv0, vk0);
-  if (ntiles > 1) issue(32, kv1, vk1);
+  const int kb = kt0 * 32;  // first key of the sweep
+  if (ntiles > 0) issue(kb, kv0, vk0);
+  if (ntiles > 1) issue(kb + 32, kv1, vk1);
   // loads complete in order: with tile 1 in flight, at most its LPT loads remain
   if (ntiles > 1) wait_vmcnt<LPT>(); else wait_vmem();
   block_sync();
@@ -2129,8 +2155,8 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     for (int j = 0; j < 3; ++j) {
       const int tt = t + j;
       if (tt < ntiles) {
-        if (tt + 2 < ntiles) issue((tt + 2) * 32, kvst(j + 2), vkst(j + 2));
-        compute(tt * 32, kvst(j), vkst(j));
+        if (tt + 2 < ntiles) issue(kb + (tt + 2) * 32, kvst(j + 2), vkst(j + 2));
+        compute(kb + tt * 32, kvst(j), vkst(j));
         // tile tt+1 has landed once only tile tt+2's loads (if any) are in flight
         if (tt + 2 < ntiles) wait_vmcnt<LPT>(); else wait_vmem();
         block_sync();
@@ -2138,7 +2164,13 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     }
   }
   if constexpr (kAgpr) agpr_settle1(dqt);
-  store_rows<D>(a.dq + qo * D, r0, a.Sq, c, g, dqt, a.scale);
+  if (part == 1) {  // second half: to the workspace, added by attn_bwd_combine_kernel
+    const int q_first = (nqt - LQ) * kBlockM;  // first row of the long tiles
+    store_rows<D>(a.pdq + size_t(bh) * size_t(LQ) * kBlockM * D, r0 - q_first, a.Sq - q_first, c, g, dqt,
+                  a.scale);
+  } else {
+    store_rows<D>(a.dq + qo * D, r0, a.Sq, c, g, dqt, a.scale);
+  }
 }
 
 template <int D>
@@ -2149,14 +2181,17 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(attn_bwd_pre_kernel<D>, dim3(unsigned(pre < 65536 ? pre : 65536)), dim3(256), 0, s, a);
   const int64_t nkv = int64_t(a.B) * a.H * ((a.Sk + kBlockM - 1) / kBlockM + a.long_tiles);
   if (nkv > 0) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(unsigned(nkv)), dim3(kThreads), 0, s, a);
-  if (a.long_tiles > 0) {
+  const int64_t nq = int64_t(a.B) * a.H * ((a.Sq + kBlockM - 1) / kBlockM + a.long_qtiles);
+  if (nq > 0) hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(unsigned(nq)), dim3(kThreads), 0, s, a);
+  if (a.long_tiles > 0 || a.long_qtiles > 0) {
+    // one pass adds every second half: after both sweeps, so it waits for neither twice
     const int64_t zr = int64_t(a.long_tiles) * kBlockM < a.Sk ? int64_t(a.long_tiles) * kBlockM : a.Sk;
-    const int64_t n4 = int64_t(a.B) * a.H * zr * (D / 4);
+    const int64_t qf = ((a.Sq + kBlockM - 1) / kBlockM - a.long_qtiles) * int64_t(kBlockM);
+    const int64_t zq = a.long_qtiles > 0 ? a.Sq - qf : 0;
+    const int64_t n4 = int64_t(a.B) * a.H * (zr > zq ? zr : zq) * (D / 4);
     const int64_t nb = (n4 + 255) / 256;
     hipLaunchKernelGGL(attn_bwd_combine_kernel<D>, dim3(unsigned(nb < 65536 ? nb : 65536)), dim3(256), 0, s, a);
   }
-  const int64_t nq = int64_t(a.B) * a.H * ((a.Sq + kBlockM - 1) / kBlockM);
-  if (nq > 0) hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(unsigned(nq)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 }  // namespace

@@ -239,7 +239,9 @@ attn_status attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v
  * the base), R = B*H*Sq rows: dO rounded to bf16 [R][d], D = sum_d dO*O [R] (fp32), lse
  * in log2 units [R] (fp32); causal only, the second-half partial dK and dV [B*H][L*128][d]
  * (fp32) of the L long key tiles (those whose causal sweep covers more than half of the
- * query rows), which attn_bwd may split between two workgroups.  Contents are scratch.
+ * query rows) and the second-half partial dQ [B*H][M*128][d] (fp32) of the M long query
+ * tiles (the last ones, whose sweep covers more than half of the longest one's keys),
+ * which attn_bwd may split between two workgroups.  Contents are scratch.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal);
 
@@ -266,8 +268,9 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal)
  * Supported: dtype ATTN_BF16 with d = 64, 128 or 256 (else ATTN_ERR_UNSUPPORTED).  All
  * pointers 16-byte aligned, buffers contiguous and not overlapping.  dO is used rounded
  * to bf16, and P and dS are rounded to bf16 as operands of the products (fp32
- * accumulation).  Asynchronous on `stream` (three launches, four when long causal key
- * tiles are split); the library allocates nothing.  Errors are returned before any launch.
+ * accumulation).  Asynchronous on `stream` (three launches, four when long causal key or
+ * query tiles are split); the library allocates nothing.  Errors are returned before any
+ * launch.
  */
 attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o,
                      const float* dout, const float* lse, float* dq, float* dk, float* dv,
@@ -275,7 +278,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o
                      float scale, int causal, attn_dtype dtype, void* stream);
 
 /* Name of a kernel attn_bwd launches: which = 0 prologue, 1 dK/dV, 2 dQ, 3 the combine
- * pass of split key tiles ("unsupported" if none). */
+ * pass of split key and query tiles ("unsupported" if none). */
 const char* attn_bwd_kernel_name(int d, attn_dtype dtype, int which);
 
 /*
