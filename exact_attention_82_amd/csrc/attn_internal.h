@@ -248,7 +248,7 @@ struct BwdArgs {
 
 // Query tiles (of 32 rows) the dK/dV sweep of 128-key tile kt visits: rows from
 // kt*128 - (Sk - Sq) on (causal), rounded down to a tile.
-inline int bwd_query_tiles(int Sq, int Sk, int kt, int causal) {
+constexpr int bwd_query_tiles(int Sq, int Sk, int kt, int causal) {
   int beg = causal ? kt * 128 - (Sk - Sq) : 0;
   beg = beg > 0 ? (beg / 32) * 32 : 0;
   return beg < Sq ? (Sq - beg + 31) / 32 : 0;
@@ -267,7 +267,7 @@ inline int bwd_long_tiles(int Sq, int Sk, int causal) {
 
 // Key tiles (of 32) the dQ sweep of 128-row query tile qt visits: up to the tile's last
 // row's diagonal (causal).
-inline int bwd_key_tiles(int Sq, int Sk, int qt, int causal) {
+constexpr int bwd_key_tiles(int Sq, int Sk, int qt, int causal) {
   int kend = Sk;
   if (causal) {
     const int last = ((qt + 1) * 128 < Sq ? (qt + 1) * 128 : Sq) - 1;
@@ -287,6 +287,33 @@ inline int bwd_long_qtiles(int Sq, int Sk, int causal) {
   int n = 0;
   while (n < nqt && bwd_key_tiles(Sq, Sk, nqt - 1 - n, 1) > (longest + 1) / 2) ++n;
   return n;
+}
+
+// Dispatch order of a causal backward launch with split tiles: the 2*nl halves of the nl
+// long tiles and the nw other tiles, merged so that longer sweeps start first (the
+// hardware hands workgroups to CUs in index order as they free up, so this is the
+// longest-first rule of list scheduling).  half_len(i) is the sweep length of either half
+// of long tile i, whole_len(j) that of other tile j; both are non-increasing.  Position m
+// gets *half = i, *part = 0/1 for a half of long tile i, or *half = -1, *part = j for other
+// tile j.  Ties go to the halves.  (A merge-path search: O(log) per call.)
+template <class HL, class WL>
+constexpr void bwd_item(int m, int nl, int nw, HL half_len, WL whole_len, int* half, int* part) {
+  const int na = 2 * nl;
+  int lo = m - nw > 0 ? m - nw : 0;
+  int hi = m < na ? m : na;
+  while (lo < hi) {  // largest a (halves before position m) consistent with the merge
+    const int a = (lo + hi + 1) / 2;
+    if (m - a >= nw || half_len((a - 1) / 2) >= whole_len(m - a)) lo = a;
+    else hi = a - 1;
+  }
+  const int a = lo, b = m - lo;
+  if (a < na && (b >= nw || half_len(a / 2) >= whole_len(b))) {
+    *half = a / 2;
+    *part = a % 2;
+  } else {
+    *half = -1;
+    *part = b;
+  }
 }
 
 struct BwdWorkspaceLayout {

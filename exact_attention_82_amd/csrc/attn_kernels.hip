@@ -1891,12 +1891,21 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int c = lane & 31, g = lane >> 5;
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
-  // Work items, longest sweeps first: the two halves of each long key tile, then the
-  // other key tiles in order.
+  // Work items, longest sweeps first: the two halves of each long key tile merged with
+  // the other key tiles by sweep length (without long tiles: the key tiles in order, which
+  // is the same rule).
   const int item = blockIdx.x / BH;
   const int L = a.long_tiles;
-  const int kt = item < 2 * L ? item / 2 : item - L;
-  const int part = item < 2 * L ? item % 2 : -1;  // -1: the whole sweep
+  int kt = item, part = -1;  // part -1: the whole sweep; 0 / 1: its first / second half
+  if (L > 0) {
+    const int nkt = ceil_div_i(a.Sk, kBlockM);
+    int hi = 0, pj = 0;
+    bwd_item(item, L, nkt - L,
+             [&](int i) { return (bwd_query_tiles(a.Sq, a.Sk, i, 1) + 1) / 2; },
+             [&](int j) { return bwd_query_tiles(a.Sq, a.Sk, L + j, 1); }, &hi, &pj);
+    kt = hi >= 0 ? hi : L + pj;
+    part = hi >= 0 ? pj : -1;
+  }
   const int kw0 = kt * kBlockM + wave * 32;  // first key of this wavefront
   const int key = kw0 + c;                   // this lane's key
   const int off = a.Sk - a.Sq;
@@ -2056,14 +2065,14 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const int LQ = a.long_qtiles;
   int qt = item, part = -1;  // part -1: the whole sweep; 0 / 1: its first / second half
   if (LQ > 0) {
-    // Longest items first: the two halves of each long (last) query tile, then the other
-    // tiles from the longest down.
-    if (item < 2 * LQ) {
-      qt = nqt - 1 - item / 2;
-      part = item % 2;
-    } else {
-      qt = nqt - 1 - LQ - (item - 2 * LQ);
-    }
+    // Longest items first: the two halves of each long (last) query tile merged with the
+    // other tiles by sweep length.
+    int hi = 0, pj = 0;
+    bwd_item(item, LQ, nqt - LQ,
+             [&](int i) { return (bwd_key_tiles(a.Sq, a.Sk, nqt - 1 - i, 1) + 1) / 2; },
+             [&](int j) { return bwd_key_tiles(a.Sq, a.Sk, nqt - 1 - LQ - j, 1); }, &hi, &pj);
+    qt = hi >= 0 ? nqt - 1 - hi : nqt - 1 - LQ - pj;
+    part = hi >= 0 ? pj : -1;
   } else if (a.causal) {  // longest (last) query tiles first, paired with short ones per CU
     const int half = (nqt + 1) / 2;
     qt = qt < half ? nqt - 1 - qt : qt - half;

@@ -163,3 +163,42 @@ def test_plan_choice_is_deterministic_with_a_margin_for_the_default(tune_probe):
         "choose 4 100 110 90 90",   # ties after the default: the first of them
     ] * 2)                           # and the same answers when asked again
     assert out == ["0", "1", "1", "0", "2"] * 2
+
+
+@pytest.fixture(scope="module")
+def bwd_order_probe(tmp_path_factory):
+    cxx = host_cxx()
+    exe = str(tmp_path_factory.mktemp("bwd") / "bwd_order_probe")
+    subprocess.run([cxx, "-std=c++17", "-O1", os.path.join(HERE, "bwd_order_probe.cpp"), "-o", exe], check=True)
+
+    def run(shapes):
+        text = "".join(f"{sq} {sk}\n" for sq, sk in shapes)
+        out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True).stdout
+        lines = out.strip().splitlines()
+        res = []
+        for kv, q in zip(lines[0::2], lines[1::2]):
+            parse = lambda l: [tuple(int(x) for x in it.split(":")) for it in l.split()[1:]]  # noqa: E731
+            res.append((parse(kv), parse(q)))
+        return res
+    return run
+
+
+def test_causal_backward_items_run_longest_first(bwd_order_probe):
+    # every work item (the two halves of each long tile, each other tile) appears exactly
+    # once, and the sweep lengths never grow along the dispatch order
+    shapes = [(8192, 8192), (700, 700), (2048, 2048), (1000, 1500), (1500, 1000), (128, 128), (300, 4096)]
+    for (sq, sk), (kv, q) in zip(shapes, bwd_order_probe(shapes)):
+        for items, ntile, nlong in ((kv, (sk + 127) // 128, None), (q, (sq + 127) // 128, None)):
+            lens = [n for _, _, n in items]
+            assert lens == sorted(lens, reverse=True), (sq, sk, items)
+            halves = {(t, p) for t, p, _ in items if p >= 0}
+            wholes = [t for t, p, _ in items if p < 0]
+            split = {t for t, _ in halves}
+            assert halves == {(t, p) for t in split for p in (0, 1)}
+            assert sorted(wholes + sorted(split)) == list(range(ntile)), (sq, sk)
+            assert len(items) == ntile + len(split)
+    (kv, q), = bwd_order_probe([(8192, 8192)])
+    # c3 shape: 32 long key tiles (sweeps of 256..132 query tiles of 32, halves 128..66) and
+    # 32 long query tiles, merged with the whole sweeps of 128 and fewer
+    assert sum(1 for _, p, _ in kv if p >= 0) == 64 and sum(1 for _, p, _ in q if p >= 0) == 64
+    assert kv[:3] == [(0, 0, 128), (0, 1, 128), (32, -1, 128)]
