@@ -254,14 +254,14 @@ constexpr int bwd_query_tiles(int Sq, int Sk, int kt, int causal) {
   return beg < Sq ? (Sq - beg + 31) / 32 : 0;
 }
 
-// Causal key tiles whose sweep covers more than half of the query tiles (a prefix: the
+// Causal key tiles whose sweep covers more than a third of the query tiles (a prefix: the
 // sweeps shrink with kt).  When a grid is resident all at once, these are swept in two
 // halves by two workgroups so that no workgroup runs much longer than the others.
 inline int bwd_long_tiles(int Sq, int Sk, int causal) {
   if (!causal) return 0;
   const int nq = (Sq + 31) / 32, nkt = (Sk + 127) / 128;
   int n = 0;
-  while (n < nkt && bwd_query_tiles(Sq, Sk, n, 1) > (nq + 1) / 2) ++n;
+  while (n < nkt && 3 * bwd_query_tiles(Sq, Sk, n, 1) > nq) ++n;
   return n;
 }
 
@@ -277,15 +277,15 @@ constexpr int bwd_key_tiles(int Sq, int Sk, int qt, int causal) {
   return (kend + 31) / 32;
 }
 
-// Causal query tiles whose dQ sweep covers more than half of the longest one (a suffix:
-// the sweeps grow with qt), swept in two halves under the same condition as the long key
-// tiles.
+// Causal query tiles whose dQ sweep covers more than a third of the longest one (a
+// suffix: the sweeps grow with qt), swept in two halves under the same condition as the
+// long key tiles.
 inline int bwd_long_qtiles(int Sq, int Sk, int causal) {
   if (!causal) return 0;
   const int nqt = (Sq + 127) / 128;
   const int longest = bwd_key_tiles(Sq, Sk, nqt - 1, 1);
   int n = 0;
-  while (n < nqt && bwd_key_tiles(Sq, Sk, nqt - 1 - n, 1) > (longest + 1) / 2) ++n;
+  while (n < nqt && 3 * bwd_key_tiles(Sq, Sk, nqt - 1 - n, 1) > longest) ++n;
   return n;
 }
 

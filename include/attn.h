@@ -238,9 +238,9 @@ attn_status attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v
  * if an argument is out of range.  Layout (each section at a multiple of 256 bytes from
  * the base), R = B*H*Sq rows: dO rounded to bf16 [R][d], D = sum_d dO*O [R] (fp32), lse
  * in log2 units [R] (fp32); causal only, the second-half partial dK and dV [B*H][L*128][d]
- * (fp32) of the L long key tiles (those whose causal sweep covers more than half of the
+ * (fp32) of the L long key tiles (those whose causal sweep covers more than a third of the
  * query rows) and the second-half partial dQ [B*H][M*128][d] (fp32) of the M long query
- * tiles (the last ones, whose sweep covers more than half of the longest one's keys),
+ * tiles (the last ones, whose sweep covers more than a third of the longest one's keys),
  * which attn_bwd may split between two workgroups.  Contents are scratch.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal);

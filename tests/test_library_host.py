@@ -184,13 +184,13 @@ def test_backward_refuses_bad_arguments_and_lays_out_its_workspace(lib):
     assert need == up(rows * d * 2) + up(rows * 4) + up(rows * 4)
     assert lib.attn_bwd_workspace_bytes(B, H, Sq, Sk, 100, 0) == 0
     assert lib.attn_bwd_workspace_bytes(B, H, Sq, Sk, d, 2) == 0
-    # causal, Sq = Sk = 700: key tiles 0-2 sweep more than half of the 22 query tiles
-    # (22, 18, 14 > 11), so the workspace also holds their second-half dK and dV; query
-    # tiles 5-2 sweep more than half of the longest dQ sweep (22, 20, 16, 12 key tiles of
-    # 32 > 11), so it holds their second-half dQ too
+    # causal, Sq = Sk = 700: key tiles 0-3 sweep more than a third of the 22 query tiles
+    # (22, 18, 14, 10 > 22/3), so the workspace also holds their second-half dK and dV;
+    # query tiles 5-1 sweep more than a third of the longest dQ sweep (22, 20, 16, 12, 8
+    # key tiles of 32 > 22/3), so it holds their second-half dQ too
     base = up(2 * 700 * d * 2) + 2 * up(2 * 700 * 4)
     assert lib.attn_bwd_workspace_bytes(1, 2, 700, 700, d, 1) == (
-        base + 2 * up(2 * 3 * 128 * d * 4) + up(2 * 4 * 128 * d * 4))
+        base + 2 * up(2 * 4 * 128 * d * 4) + up(2 * 5 * 128 * d * 4))
     assert lib.attn_bwd_workspace_bytes(1, 2, 700, 700, d, 0) == base
     DO, DQ, DK, DV, W = 0x60000, 0x70000, 0x80000, 0x90000, 0xA0000
 

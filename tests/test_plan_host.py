@@ -198,7 +198,9 @@ def test_causal_backward_items_run_longest_first(bwd_order_probe):
             assert sorted(wholes + sorted(split)) == list(range(ntile)), (sq, sk)
             assert len(items) == ntile + len(split)
     (kv, q), = bwd_order_probe([(8192, 8192)])
-    # c3 shape: 32 long key tiles (sweeps of 256..132 query tiles of 32, halves 128..66) and
-    # 32 long query tiles, merged with the whole sweeps of 128 and fewer
-    assert sum(1 for _, p, _ in kv if p >= 0) == 64 and sum(1 for _, p, _ in q if p >= 0) == 64
-    assert kv[:3] == [(0, 0, 128), (0, 1, 128), (32, -1, 128)]
+    # c3 shape: 43 long key tiles (sweeps of 256..88 query tiles of 32, more than a third
+    # of 256; halves 128..44) and 43 long query tiles, merged with the whole sweeps of 84
+    # and fewer
+    assert sum(1 for _, p, _ in kv if p >= 0) == 86 and sum(1 for _, p, _ in q if p >= 0) == 86
+    assert kv[:3] == [(0, 0, 128), (0, 1, 128), (1, 0, 126)]
+    assert kv.index((43, -1, 84)) == kv.index((22, 1, 84)) + 1   # ties: the halves first
