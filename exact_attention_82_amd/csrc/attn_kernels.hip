@@ -1209,8 +1209,14 @@ void attn_fwd_kernel(FwdArgs p) {
         if (act_2) pipe.qk(s_next, kb, qop);
         if (act_t) pipe.pv(ov(), s_cur, pcur, vb);
         if (act_1) {
+          // the main loop's lazy softmax, with the mask where the tile needs one
           if (needs_mask(k0 + BN)) mask_tile<BN>(s_cur, k0 + BN, kend, row, off, p.causal, g);
-          softmax_tile<DT, BN, NACC>(s_cur, pnext, oacc, m_run, l_run, c_run, sl2);
+          f32x16_t pr[NKB];
+          float ls = softmax_exp_ref<BN>(s_cur, pr, m_run, sl2);
+          if (__builtin_amdgcn_ballot_w64(!(ls <= kSumCap)))
+            ls = softmax_redo<BN, NACC>(s_cur, pr, oacc, m_run, l_run, c_run, sl2);
+          l_run += ls;
+          c_run += pack_bf16<BN>(pr, pnext);
         }
         finish_d();
       };
