@@ -285,8 +285,10 @@ const char* attn_bwd_kernel_name(int d, attn_dtype dtype, int which);
  * Launch plan queries.  num_splits = 0 describes attn_fwd; num_splits >= 1 describes
  * attn_fwd_splitkv with that many chunks.  A call launches one four-wavefront workgroup
  * per 128 query rows (times num_splits), except causal bf16 calls with d <= 128 whose
- * tile pairs fit one workgroup per CU: those launch one eight-wavefront workgroup per
- * pair of 128-row tiles (t, last - t), 256 query rows.  Plans depend on the current
+ * tiles outnumber the CUs but whose tile pairs fit one workgroup per CU: those launch one
+ * eight-wavefront workgroup per pair of 128-row tiles (t, last - t), 256 query rows.
+ * (Grids of at most one tile per CU launch eight-wavefront workgroups of 128 query rows
+ * whose two halves split the keys, with the same count.)  Plans depend on the current
  * device's CU count (a HIP query) and on a plan stored for the shape by attn_tune or
  * attn_plan_set, if any.
  */

@@ -26,7 +26,7 @@ CASES = [
     ("bf16", 2, 3, 300, 300, 128, True),
     ("bf16", 1, 4, 257, 513, 256, True),
     ("bf16", 4, 16, 640, 640, 128, False),   # 320 workgroups: plain kernel
-    ("bf16", 1, 8, 2048, 2048, 128, True),   # causal tile pairs
+    ("bf16", 1, 40, 1024, 1024, 128, True),  # causal tile pairs (320 tiles, 160 pairs)
     ("fp8", 1, 4, 200, 1000, 128, False),
     ("f32", 1, 2, 130, 97, 64, True),
 ]

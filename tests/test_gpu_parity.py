@@ -307,19 +307,30 @@ def test_splitkv_counts_with_empty_chunks(dtype, causal):
 
 # ------------------------------------------------------------------ causal schedules
 def test_causal_tile_pairs_plan_and_parity():
-    """A causal bf16 grid whose tile pairs fit one workgroup per CU runs the pair kernel
-    (two groups per workgroup split each pair's keys and merge); odd tile count (the
-    middle tile pairs with itself), Sq != Sk, ragged last tile."""
+    """A causal bf16 grid with more tiles than CUs whose tile pairs fit one workgroup per
+    CU runs the pair kernel (two groups per workgroup split each pair's keys and merge);
+    a grid of at most one tile per CU runs two groups per tile instead.  Parity of the
+    pair kernel (set explicitly on the small grid): odd tile count (the middle tile pairs
+    with itself), Sq != Sk, ragged last tile."""
     B, H, Sq, Sk, d = 1, 3, 1100, 1500, 128
     nqt = -(-Sq // 128)
-    assert ea.attn_kernel_name(B, H, Sq, Sk, d, 1, ea.ATTN_BF16).startswith("attn_fwd_causal_pairs_bf16_d128")
-    assert ea.attn_block_m(B, H, Sq, Sk, d, 1, ea.ATTN_BF16) == 256
-    assert ea.attn_num_workgroups(B, H, Sq, Sk, d, 1, ea.ATTN_BF16) == B * H * ((nqt + 1) // 2)
+    assert ea.attn_kernel_name(1, 40, Sq, Sk, d, 1, ea.ATTN_BF16).startswith("attn_fwd_causal_pairs_bf16_d128")
+    assert ea.attn_block_m(1, 40, Sq, Sk, d, 1, ea.ATTN_BF16) == 256
+    assert ea.attn_num_workgroups(1, 40, Sq, Sk, d, 1, ea.ATTN_BF16) == 40 * ((nqt + 1) // 2)
+    assert ea.attn_kernel_name(B, H, Sq, Sk, d, 1, ea.ATTN_BF16).startswith("attn_fwd_dual_bf16_d128")
     inp = si.make_attention_inputs(B, H, Sq, Sk, d, seed=21, dtype="bf16", hot_row_frac=0.01)
     sc = scale_for(d)
-    o, lse = _run_fwd(inp, sc, True)
     ro, rl = oracle.attention(inp.q64, inp.k64, inp.v64, sc, True)
+    try:
+        ea.attn_plan_set(B, H, Sq, Sk, d, 1, ea.ATTN_BF16, 2)
+        assert ea.attn_kernel_name(B, H, Sq, Sk, d, 1, ea.ATTN_BF16).startswith("attn_fwd_causal_pairs_bf16_d128")
+        assert ea.attn_num_workgroups(B, H, Sq, Sk, d, 1, ea.ATTN_BF16) == B * H * ((nqt + 1) // 2)
+        o, lse = _run_fwd(inp, sc, True)
+    finally:
+        ea.attn_plan_clear()
     check("causal pairs bf16 (1, 3, 1100, 1500)", o, lse, ro, rl, "bf16")
+    o, lse = _run_fwd(inp, sc, True)   # the rule's plan: two groups per tile
+    check("causal two groups bf16 (1, 3, 1100, 1500)", o, lse, ro, rl, "bf16")
 
 
 def test_small_grids_run_two_groups_per_workgroup():

@@ -57,14 +57,18 @@ def test_small_grids_use_two_groups(probe):
 def test_causal_orders(probe):
     out = probe([(1, 2, 700, 64, 1, FP8, 256),     # resident grid: complementary tiles
                  (4, 40, 700, 64, 1, BF16, 256),   # 960 workgroups: longest first
-                 (1, 3, 1100, 128, 1, BF16, 256),  # tile pairs (odd tile count)
+                 (1, 40, 1100, 128, 1, BF16, 256), # 360 tiles, 200 pairs: tile pairs (odd count)
                  (1, 4, 8192, 256, 1, BF16, 256),  # d = 256: no pair kernel; 1 per CU fits
-                 (1, 8, 8192, 256, 1, BF16, 256)]) # ... 2 per CU do not: longest first
+                 (1, 8, 8192, 256, 1, BF16, 256),  # ... 2 per CU do not: longest first
+                 (1, 3, 1100, 128, 1, BF16, 256),  # 27 tiles, one per CU: two groups per tile
+                 (1, 16, 2048, 64, 1, BF16, 256),  # 256 tiles = the CUs: two groups per tile
+                 (1, 16, 2048, 128, 1, FP8, 256)]) # fp8 d = 128 too
     assert out[0][1] == 1
     assert out[1][1] == 0
-    assert out[2] == (256, 2, 1)
+    assert out[2][:2] == (256, 2)
     assert out[3][1] == 1
     assert out[4][1] == 0
+    assert out[5][:2] == (128, 3) and out[6][:2] == (128, 3) and out[7][:2] == (128, 3)
 
 
 def test_without_a_device_query_plans_are_plain(probe):
@@ -125,11 +129,12 @@ def tune_probe(tmp_path_factory):
 
 
 def test_tuning_candidates_are_the_legal_plans_default_first(tune_probe):
-    # causal bf16 d=128, B=1, H=4, S=1000 on 256 CUs: the rule picks tile pairs (plan 2);
-    # schedules 0 and 3 come with head groups 1, 2, 4 (dividing B*H = 4), 1 alone
+    # causal bf16 d=128, B=1, H=4, S=1000 on 256 CUs: 32 tiles, one per CU, so the rule
+    # picks two groups per tile (plan 3); schedules 0 and 3 come with head groups 1, 2, 4
+    # (dividing B*H = 4), 1 and 2 alone
     out = tune_probe(["cand 1 4 1000 128 1 1 256"])
     cand = [int(x) for x in out[0].split()]
-    assert cand[0] == 2
+    assert cand[0] == 3
     assert sorted(cand) == sorted([0, 4, 8, 1, 2, 3, 7, 11])
     # non-causal fp32: no dual, pair or complementary schedule; B*H = 6 allows head groups 1, 2
     cand = [int(x) for x in tune_probe(["cand 2 3 512 64 0 0 256"])[0].split()]
