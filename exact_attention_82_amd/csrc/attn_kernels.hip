@@ -2079,9 +2079,8 @@ void attn_bwd_dq_kernel(BwdArgs a) {
              [&](int j) { return bwd_key_tiles(a.Sq, a.Sk, nqt - 1 - LQ - j, 1); }, &hi, &pj);
     qt = hi >= 0 ? nqt - 1 - hi : nqt - 1 - LQ - pj;
     part = hi >= 0 ? pj : -1;
-  } else if (a.causal) {  // longest (last) query tiles first, paired with short ones per CU
-    const int half = (nqt + 1) / 2;
-    qt = qt < half ? nqt - 1 - qt : qt - half;
+  } else if (a.causal) {  // longest (last) query tiles first
+    qt = nqt - 1 - qt;
   }
   const int r0 = qt * kBlockM + wave * 32;
   const int row = r0 + c;  // this lane's query row
