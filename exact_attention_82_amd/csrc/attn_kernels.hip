@@ -870,9 +870,11 @@ __device__ __forceinline__ void interleave_pv() {
 }
 
 // Interleave for the deferred bf16 main loop: each of the iteration's MFMAs
-// (S^T of tile t+2, then P(t) V(t)) is followed by a share of the VALU work on tile
-// t+1 -- exponentials, row sum, bf16 packing and the sum of the packed values -- none
-// of which the MFMAs depend on.
+// (S^T of tile t+2, then P(t) V(t)) is followed by two VALU instructions of the work on
+// tile t+1 -- exponentials, row sum, bf16 packing and the sum of the packed values, none
+// of which the MFMAs depend on -- and what remains of that work follows the last MFMA.
+// (Two per MFMA measured 1.7-3 % faster at d = 64 and 128 than spreading all of it
+// evenly, i.e. 4 or 8 per MFMA; one, three, none, or a block of it first were slower.)
 template <int D, int BN>
 __device__ __forceinline__ void interleave_deferred() {
   constexpr int NKB = BN / 32;
@@ -880,7 +882,8 @@ __device__ __forceinline__ void interleave_deferred() {
   constexpr int NV = NKB * (48 + 16);                       // VALU per iteration
   constexpr int NR = NKB * (D / 16) + NKB * 2 * (D / 32) * 2;  // LDS operand reads
   __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-  sched_pairs<NM, 0x8, 1, 0x2, (NV + NM - 1) / NM>();
+  sched_pairs<NM, 0x8, 1, 0x2, 2>();
+  __builtin_amdgcn_sched_group_barrier(0x2, NV, 0);
 }
 
 // Largest finite E4M3 value.
