@@ -2032,16 +2032,6 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void attn_bwd_combine_kernel(BwdArgs a) {
-  const int rows = min(a.Sk, a.long_tiles * kBlockM);  // per (batch, head)
-  const int64_t n4 = int64_t(a.B) * a.H * rows * (D / 4);
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += int64_t(gridDim.x) * 256) {
-    const int64_t r = i / (D / 4), col = (i % (D / 4)) * 4;
-    const int64_t bh = r / rows, kr = r % rows;
-    const size_t o = size_t(bh * a.Sk + kr) * D + col;
-    const size_t w = size_t(bh * int64_t(a.long_tiles) * kBlockM + kr) * D + col;
-    *reinterpret_cast<f32x4_t*>(a.dk + o) += *reinterpret_cast<const f32x4_t*>(a.pdk + w);
-    *reinterpret_cast<f32x4_t*>(a.dv + o) += *reinterpret_cast<const f32x4_t*>(a.pdv + w);
-  }
   // the long query tiles are the last ones: rows [q_first, Sq) of every (batch, head)
   const int q_first = (ceil_div_i(a.Sq, kBlockM) - a.long_qtiles) * kBlockM;
   const int qrows = a.Sq - q_first;
@@ -2052,6 +2042,43 @@ void attn_bwd_combine_kernel(BwdArgs a) {
     const size_t o = size_t(bh * a.Sq + q_first + qr) * D + col;
     const size_t w = size_t(bh * int64_t(a.long_qtiles) * kBlockM + qr) * D + col;
     *reinterpret_cast<f32x4_t*>(a.dq + o) += *reinterpret_cast<const f32x4_t*>(a.pdq + w);
+  }
+}
+
+// dK and dV of the long key tiles: the first half's (in dk, dv) plus the second half's
+// (pdk, pdv), in that order.  The dQ launch runs this in the workgroups past its own
+// items: the dispatcher starts them last, on the CUs the shortest dQ sweeps leave idle,
+// and the dK/dV launch before it has finished both halves.  Each thread keeps kCombineU
+// elements' loads in flight at once.
+constexpr int kCombineU = 4;
+template <int D>
+__device__ __forceinline__ void combine_kv(const BwdArgs& a, int64_t first, int64_t stride) {
+  const int rows = min(a.Sk, a.long_tiles * kBlockM);  // per (batch, head)
+  const int64_t n4 = int64_t(a.B) * a.H * rows * (D / 4);
+  for (int64_t base = first; base < n4; base += stride * kCombineU) {
+    f32x4_t k0[kCombineU], k1[kCombineU], v0[kCombineU], v1[kCombineU];
+    size_t oo[kCombineU];
+#pragma unroll
+    for (int j = 0; j < kCombineU; ++j) {
+      const int64_t i = base + j * stride;
+      if (i < n4) {
+        const int64_t r = i / (D / 4), col = (i % (D / 4)) * 4;
+        const int64_t bh = r / rows, kr = r % rows;
+        oo[j] = size_t(bh * a.Sk + kr) * D + col;
+        const size_t w = size_t(bh * int64_t(a.long_tiles) * kBlockM + kr) * D + col;
+        k0[j] = *reinterpret_cast<const f32x4_t*>(a.dk + oo[j]);
+        k1[j] = *reinterpret_cast<const f32x4_t*>(a.pdk + w);
+        v0[j] = *reinterpret_cast<const f32x4_t*>(a.dv + oo[j]);
+        v1[j] = *reinterpret_cast<const f32x4_t*>(a.pdv + w);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineU; ++j) {
+      if (base + j * stride < n4) {
+        *reinterpret_cast<f32x4_t*>(a.dk + oo[j]) = k0[j] + k1[j];
+        *reinterpret_cast<f32x4_t*>(a.dv + oo[j]) = v0[j] + v1[j];
+      }
+    }
   }
 }
 
@@ -2069,9 +2096,15 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const int c = lane & 31, g = lane >> 5;
   const int BH = a.B * a.H;
   const int nqt = ceil_div_i(a.Sq, kBlockM);
+  const int LQ = a.long_qtiles;
+  const int nitems = BH * (nqt + LQ);
+  if (int(blockIdx.x) >= nitems) {  // the dK/dV combine workgroups (before any barrier)
+    combine_kv<D>(a, int64_t(int(blockIdx.x) - nitems) * 256 + tid,
+                  int64_t(int(gridDim.x) - nitems) * 256);
+    return;
+  }
   const int bh = blockIdx.x % BH;
   const int item = blockIdx.x / BH;
-  const int LQ = a.long_qtiles;
   int qt = item, part = -1;  // part -1: the whole sweep; 0 / 1: its first / second half
   if (LQ > 0) {
     // Longest items first: the two halves of each long (last) query tile merged with the
@@ -2199,13 +2232,19 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int64_t nkv = int64_t(a.B) * a.H * ((a.Sk + kBlockM - 1) / kBlockM + a.long_tiles);
   if (nkv > 0) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(unsigned(nkv)), dim3(kThreads), 0, s, a);
   const int64_t nq = int64_t(a.B) * a.H * ((a.Sq + kBlockM - 1) / kBlockM + a.long_qtiles);
-  if (nq > 0) hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(unsigned(nq)), dim3(kThreads), 0, s, a);
-  if (a.long_tiles > 0 || a.long_qtiles > 0) {
-    // one pass adds every second half: after both sweeps, so it waits for neither twice
+  // dK/dV of the split key tiles are combined by workgroups appended to the dQ grid (one
+  // per kCombineU x 256 elements, at most 512); the dQ halves by one pass after it.
+  int64_t ncomb = 0;
+  if (a.long_tiles > 0) {
     const int64_t zr = int64_t(a.long_tiles) * kBlockM < a.Sk ? int64_t(a.long_tiles) * kBlockM : a.Sk;
+    const int64_t n4 = int64_t(a.B) * a.H * zr * (D / 4);
+    ncomb = (n4 + 256 * kCombineU - 1) / (256 * kCombineU);
+    ncomb = ncomb < 512 ? ncomb : 512;
+  }
+  if (nq > 0) hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(unsigned(nq + ncomb)), dim3(kThreads), 0, s, a);
+  if (a.long_qtiles > 0) {
     const int64_t qf = ((a.Sq + kBlockM - 1) / kBlockM - a.long_qtiles) * int64_t(kBlockM);
-    const int64_t zq = a.long_qtiles > 0 ? a.Sq - qf : 0;
-    const int64_t n4 = int64_t(a.B) * a.H * (zr > zq ? zr : zq) * (D / 4);
+    const int64_t n4 = int64_t(a.B) * a.H * (a.Sq - qf) * (D / 4);
     const int64_t nb = (n4 + 255) / 256;
     hipLaunchKernelGGL(attn_bwd_combine_kernel<D>, dim3(unsigned(nb < 65536 ? nb : 65536)), dim3(256), 0, s, a);
   }

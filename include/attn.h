@@ -268,8 +268,8 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal)
  * Supported: dtype ATTN_BF16 with d = 64, 128 or 256 (else ATTN_ERR_UNSUPPORTED).  All
  * pointers 16-byte aligned, buffers contiguous and not overlapping.  dO is used rounded
  * to bf16, and P and dS are rounded to bf16 as operands of the products (fp32
- * accumulation).  Asynchronous on `stream` (three launches, four when long causal key or
- * query tiles are split); the library allocates nothing.  Errors are returned before any
+ * accumulation).  Asynchronous on `stream` (three launches, four when long causal query
+ * tiles are split); the library allocates nothing.  Errors are returned before any
  * launch.
  */
 attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o,
@@ -277,8 +277,9 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const float* o
                      void* ws, size_t ws_bytes, int B, int H, int Sq, int Sk, int d,
                      float scale, int causal, attn_dtype dtype, void* stream);
 
-/* Name of a kernel attn_bwd launches: which = 0 prologue, 1 dK/dV, 2 dQ, 3 the combine
- * pass of split key and query tiles ("unsupported" if none). */
+/* Name of a kernel attn_bwd launches: which = 0 prologue, 1 dK/dV, 2 dQ (whose last
+ * workgroups also add the halves of split key tiles), 3 the combine pass of split query
+ * tiles ("unsupported" if none). */
 const char* attn_bwd_kernel_name(int d, attn_dtype dtype, int which);
 
 /*
