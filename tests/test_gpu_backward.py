@@ -220,6 +220,30 @@ def test_backward_one_head_at_training_size():
                  label="bwd 1x4x2048 d=128 causal, head 3")
 
 
+def test_backward_split_sweeps_at_sixteen_heads():
+    """B=1, H=16, S=2048, d=128, causal: the dK/dV and dQ grids (256 workgroups each) are
+    resident at once, so the long key and query sweeps run in two halves, and the dK/dV
+    halves (16 heads x 11 long key tiles) are added by the last workgroups of the dQ launch
+    in more than one round per thread.  Heads 0 and 15 compared in full."""
+    B, H, S, d = 1, 16, 2048, 128
+    inp, do = _inputs(B, H, S, S, d, seed=12)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    q, k, v = upload(inp)
+    o_t, l_t = ea.attn_fwd(q, k, v, scale=scale, causal=True)
+    dt = torch.from_numpy(do).cuda()
+    dq, dk, dv = (_np(x) for x in ea.attn_bwd(q, k, v, o_t, l_t, dt, scale=scale, causal=True))
+    assert all(np.isfinite(x).all() for x in (dq, dk, dv))
+    o_ref, l_ref = _oracle_fwd(inp, scale, True)
+    eo = float(np.abs(_np(o_t) - o_ref).max())
+    el = float(np.abs(_np(l_t) - l_ref).max())
+    for h in (0, H - 1):
+        one = si.AttentionInputs("bf16", 1, 1, S, S, d, 12, None, None, None,
+                                 inp.q64[:, h:h + 1], inp.k64[:, h:h + 1], inp.v64[:, h:h + 1])
+        _check_heads(one, do[:, h:h + 1], scale, True,
+                     (dq[:, h:h + 1], dk[:, h:h + 1], dv[:, h:h + 1]), extra_d=eo, extra_lse=el,
+                     label=f"bwd 1x16x2048 d=128 causal, head {h}")
+
+
 def test_backward_refuses_what_it_does_not_support():
     inp, do = _inputs(1, 1, 64, 64, 64, seed=1)
     q, k, v = upload(inp)
