@@ -1298,8 +1298,8 @@ void attn_fwd_kernel(FwdArgs p) {
       P::template wait_loads<NS - 2>();
       block_sync();
     };
-    // Main part: tiles with a successor that are visible to every row of the group
-    // (no mask, every wavefront active).  One straight-line block per tile.
+    // Main part: tiles visible to every row of the group (no mask, every wavefront
+    // active).  One straight-line block per tile.
     auto step_full = [&](int t, uint8_t* kdst, uint8_t* vdst, const uint8_t* kb, const uint8_t* vb,
                          f32x16_t (&s_cur)[NKB], f32x16_t (&s_next)[NKB]) __attribute__((always_inline)) {
       const int k0 = kbeg + t * BN;
@@ -1388,8 +1388,10 @@ void attn_fwd_kernel(FwdArgs p) {
     };
     // Tiles [0, nfull) are full: below every row's diagonal (causal) and before kend;
     // nfull is rounded down to a multiple of U so that both loops start on stage 0
-    // with the first score buffer, unrolled with constant stage indices.
-    int nfull = ntiles - 1;
+    // with the first score buffer, unrolled with constant stage indices.  The last tile
+    // of the range may be one of them: the S^T its step computes for the next tile then
+    // comes from a stage the ring filled with zeros and is never read.
+    int nfull = ntiles;
     {
       const int lim_end = (kend - kbeg) / BN;  // tiles ending at or before kend
       nfull = min(nfull, lim_end);
