@@ -333,6 +333,26 @@ def test_causal_tile_pairs_plan_and_parity():
     check("causal two groups bf16 (1, 3, 1100, 1500)", o, lse, ro, rl, "bf16")
 
 
+@pytest.mark.parametrize("B,H,Sq,Sk", [(1, 2, 1100, 1500), (2, 1, 900, 700), (1, 3, 1024, 1024)])
+def test_causal_tile_pairs_head_dim_64(B, H, Sq, Sk):
+    """The d = 64 pair kernel (64-key tiles), set explicitly: odd and even tile counts,
+    Sq > Sk (rows with no visible key at the top), Sq < Sk, ragged last tile, and tile
+    ranges whose key-tile counts are and are not multiples of the ring's four stages."""
+    d = 64
+    inp = si.make_attention_inputs(B, H, Sq, Sk, d, seed=40 + Sq % 97, dtype="bf16", hot_row_frac=0.01)
+    sc = scale_for(d)
+    ro, rl = oracle.attention(inp.q64, inp.k64, inp.v64, sc, True)
+    nqt = -(-Sq // 128)
+    try:
+        ea.attn_plan_set(B, H, Sq, Sk, d, 1, ea.ATTN_BF16, 2)
+        assert ea.attn_kernel_name(B, H, Sq, Sk, d, 1, ea.ATTN_BF16).startswith("attn_fwd_causal_pairs_bf16_d64")
+        assert ea.attn_num_workgroups(B, H, Sq, Sk, d, 1, ea.ATTN_BF16) == B * H * ((nqt + 1) // 2)
+        o, lse = _run_fwd(inp, sc, True)
+    finally:
+        ea.attn_plan_clear()
+    check(f"causal pairs bf16 d=64 {(B, H, Sq, Sk)}", o, lse, ro, rl, "bf16")
+
+
 def test_small_grids_run_two_groups_per_workgroup():
     """Grids of at most one workgroup per CU split each tile's keys between two groups
     (the split-KV chunks too); parity of those kernels is covered by every small-shape
