@@ -1888,9 +1888,16 @@ __device__ __forceinline__ f32x16_t rows_product_reg(const uint8_t* xt, int xv,
 // and 256 registers per wavefront).  Causal: key tile kt sees the queries from
 // kt*128 - (Sk - Sq) on, so workgroups i and i + grid/2, which share a CU, take
 // complementary key tiles.
+// Wavefronts per SIMD of the backward kernels: the products of one tile form one dependent
+// chain per wavefront, so more wavefronts per SIMD fill more of its gaps.  At d = 64 the
+// dK/dV kernel fits three in the register file (at most 168 registers; 33 KB of LDS per
+// workgroup) and the dQ kernel four (128 registers, 24 KB); d = 128 two (three would spill
+// in dQ), d = 256 one.
+constexpr int bwd_waves(int d, bool dq) { return d >= 256 ? 1 : d == 64 ? (dq ? 4 : 3) : 2; }
+
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
+                          amdgpu_waves_per_eu(bwd_waves(D, false), bwd_waves(D, false))))
 void attn_bwd_dkdv_kernel(BwdArgs a) {
   using Op = Traits<DT_BF16>::Op;
   using G = DmaGeo<DT_BF16, D, 32>;
@@ -2086,7 +2093,7 @@ __device__ __forceinline__ void combine_kv(const BwdArgs& a, int64_t first, int6
 
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
+                          amdgpu_waves_per_eu(bwd_waves(D, true), bwd_waves(D, true))))
 void attn_bwd_dq_kernel(BwdArgs a) {
   using Op = Traits<DT_BF16>::Op;
   using G = DmaGeo<DT_BF16, D, 32>;
