@@ -444,8 +444,9 @@ const char* attn_kernel_name(int B, int H, int Sq, int Sk, int d, int causal, at
                              int num_splits) {
   if (attn_block_m(B, H, Sq, Sk, d, causal, dtype, num_splits) == 0) return "unsupported";
   if (num_splits >= 1)
-    return attn::fwd_kernel_name(dtype, d, 1, splitkv_schedule(B, H, Sq, d, dtype, num_splits));
-  return attn::fwd_kernel_name(dtype, d, 0, plan_for(B, H, Sq, Sk, d, causal, dtype).pair_order);
+    return attn::fwd_kernel_name(dtype, d, 1, splitkv_schedule(B, H, Sq, d, dtype, num_splits),
+                                 static_cast<int>(ceil_div(Sk, num_splits)));
+  return attn::fwd_kernel_name(dtype, d, 0, plan_for(B, H, Sq, Sk, d, causal, dtype).pair_order, Sk);
 }
 
 // ---------------------------------------------------------------- shape-keyed tuning

@@ -15,8 +15,22 @@ constexpr int kBlockM = 128;      // query rows per workgroup
 constexpr int kMaxPrefetchKeys = 512;  // keys past the end a sweep may request (ring depth)
 
 // Keys per tile of the key sweep, by element type and head dim.
+// Keys per tile of the four-wavefront kernels (one group per workgroup) ...
 constexpr int block_n(int dtype, int d) {
-  return dtype == 0 ? 32 : dtype == 1 ? (d == 64 ? 64 : 32) : 64;  // fp32 | bf16 | fp8
+  (void)d;
+  return dtype == 0 ? 32 : dtype == 1 ? 32 : 64;  // fp32 | bf16 | fp8
+}
+// (bf16 d = 64 sweeps 32-key tiles with three workgroups per CU when a workgroup sweeps at
+// most kShortSweep keys, and 64-key tiles with two beyond: the third workgroup pays for
+// the extra barriers of the smaller tiles on short sweeps, not on long ones)
+constexpr int kShortSweep = 4096;
+constexpr int block_n_for(int dtype, int d, int sweep_keys) {
+  return (dtype == 1 && d == 64 && sweep_keys > kShortSweep) ? 64 : block_n(dtype, d);
+}
+// ... and of the two-group kernels (tile pairs, two groups per tile), whose hand-off
+// between the groups needs a 64-key stage at d = 64.
+constexpr int block_n_two_groups(int dtype, int d) {
+  return dtype == 1 ? (d == 64 ? 64 : 32) : 64;
 }
 
 struct FwdArgs {
@@ -355,6 +369,6 @@ int device_cu_count();
 // *hip_err set if the lookup fails).
 constexpr size_t kNoallocScratchBytes = size_t(32) << 20;  // ATTN_NOALLOC_SCRATCH_BYTES
 void* noalloc_scratch(int* hip_err);
-const char* fwd_kernel_name(int dtype, int d, int split_mode, int sched);
+const char* fwd_kernel_name(int dtype, int d, int split_mode, int sched, int sweep_keys);
 
 }  // namespace attn

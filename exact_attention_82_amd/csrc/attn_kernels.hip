@@ -747,8 +747,13 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], PTile<DT, B
 }
 
 // Wavefronts per SIMD the register budget allows: two (256 registers each) unless a
-// wavefront holds a d = 256 accumulator or fp32 operands.
+// wavefront holds a d = 256 accumulator or fp32 operands; three (168 registers) for the
+// bf16 d = 64 four-wavefront kernels, whose 32-key tiles leave 32 KB of LDS per workgroup
+// and whose VALU-heavy sweep gains from a third wavefront beside each MFMA stream.
 constexpr int waves_per_eu(int dt, int d) { return (d >= 256 || dt == DT_F32) ? 1 : 2; }
+constexpr int fwd_waves(int dt, int d, int bn, bool two_groups) {
+  return (dt == DT_BF16 && d == 64 && bn == 32 && !two_groups) ? 3 : waves_per_eu(dt, d);
+}
 
 // ================================================================== tile pipeline
 // Uniform interface over the two ways tiles reach LDS.  issue_*: start the loads of a
@@ -909,7 +914,8 @@ constexpr bool two_groups(int mode) { return mode == kPairs || mode == kDualPlai
 template <int DT, int D, int BN, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads * (two_groups(MODE) ? 2 : 1),
                                                       kThreads * (two_groups(MODE) ? 2 : 1)),
-                          amdgpu_waves_per_eu(waves_per_eu(DT, D), waves_per_eu(DT, D))))
+                          amdgpu_waves_per_eu(fwd_waves(DT, D, BN, two_groups(MODE)),
+                                              fwd_waves(DT, D, BN, two_groups(MODE)))))
 void attn_fwd_kernel(FwdArgs p) {
   using TR = Traits<DT>;
   using P = Pipe<DT, D, BN, kWaves>;
@@ -1667,12 +1673,12 @@ void attn_merge_kernel(MergeArgs a) {
 
 template <int DT, int D>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
-  constexpr int BN = block_n(DT, D);
+  constexpr int BN = block_n(DT, D), BN2 = block_n_two_groups(DT, D);
   const int64_t nqt = (a.Sq + kBlockM - 1) / kBlockM;
   if constexpr (pairs_supported(DT, D)) {
     if (a.pair_order == 2 && !a.split_mode && a.causal) {
       const int64_t nwg = int64_t(a.B) * a.H * ((nqt + 1) / 2);
-      hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN, kPairs>), dim3(unsigned(nwg)), dim3(2 * kThreads), 0, s, a);
+      hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN2, kPairs>), dim3(unsigned(nwg)), dim3(2 * kThreads), 0, s, a);
       return hipGetLastError();
     }
   }
@@ -1680,9 +1686,18 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   if constexpr (dual_supported(DT, D)) {
     if (a.pair_order == 3) {
       if (a.split_mode)
-        hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN, kDualSplit>), dim3(unsigned(nwg)), dim3(2 * kThreads), 0, s, a);
+        hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN2, kDualSplit>), dim3(unsigned(nwg)), dim3(2 * kThreads), 0, s, a);
       else
-        hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN, kDualPlain>), dim3(unsigned(nwg)), dim3(2 * kThreads), 0, s, a);
+        hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BN2, kDualPlain>), dim3(unsigned(nwg)), dim3(2 * kThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (DT == DT_BF16 && D == 64) {
+    if (a.chunk > kShortSweep) {  // long sweeps: 64-key tiles, two workgroups per CU
+      if (a.split_mode)
+        hipLaunchKernelGGL((attn_fwd_kernel<DT, D, 64, kSplit>), dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_fwd_kernel<DT, D, 64, kPlain>), dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
       return hipGetLastError();
     }
   }
@@ -2344,7 +2359,7 @@ int device_cu_count() {
   return n;
 }
 
-const char* fwd_kernel_name(int dtype, int d, int split_mode, int sched) {
+const char* fwd_kernel_name(int dtype, int d, int split_mode, int sched, int sweep_keys) {
   if (sched == 2 && pairs_supported(dtype, d))
     return d == 64 ? "attn_fwd_causal_pairs_bf16_d64_bm256_bn64" : "attn_fwd_causal_pairs_bf16_d128_bm256_bn32";
   if (sched == 3 && dual_supported(dtype, d)) {
@@ -2358,13 +2373,15 @@ const char* fwd_kernel_name(int dtype, int d, int split_mode, int sched) {
       {{"attn_fwd_f32_d64_bm128_bn32", "attn_fwd_splitkv_f32_d64_bm128_bn32"},
        {"attn_fwd_f32_d128_bm128_bn32", "attn_fwd_splitkv_f32_d128_bm128_bn32"},
        {"attn_fwd_f32_d256_bm128_bn32", "attn_fwd_splitkv_f32_d256_bm128_bn32"}},
-      {{"attn_fwd_bf16_d64_bm128_bn64", "attn_fwd_splitkv_bf16_d64_bm128_bn64"},
+      {{"attn_fwd_bf16_d64_bm128_bn32", "attn_fwd_splitkv_bf16_d64_bm128_bn32"},
        {"attn_fwd_bf16_d128_bm128_bn32", "attn_fwd_splitkv_bf16_d128_bm128_bn32"},
        {"attn_fwd_bf16_d256_bm128_bn32", "attn_fwd_splitkv_bf16_d256_bm128_bn32"}},
       {{"attn_fwd_fp8_d64_bm128_bn64", "attn_fwd_splitkv_fp8_d64_bm128_bn64"},
        {"attn_fwd_fp8_d128_bm128_bn64", "attn_fwd_splitkv_fp8_d128_bm128_bn64"},
        {"attn_fwd_fp8_d256_bm128_bn64", "attn_fwd_splitkv_fp8_d256_bm128_bn64"}}};
   const int di = d == 64 ? 0 : d == 128 ? 1 : 2;
+  if (block_n_for(dtype, d, sweep_keys) == 64 && dtype == DT_BF16)
+    return split_mode ? "attn_fwd_splitkv_bf16_d64_bm128_bn64" : "attn_fwd_bf16_d64_bm128_bn64";
   return names[dtype][di][split_mode ? 1 : 0];
 }
 

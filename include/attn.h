@@ -297,7 +297,9 @@ const char* attn_bwd_kernel_name(int d, attn_dtype dtype, int which);
 int attn_block_m(int B, int H, int Sq, int Sk, int d, int causal, attn_dtype dtype,
                  int num_splits);
 
-/* Keys per tile of the key sweep of the four-wavefront kernel for (d, dtype), or 0. */
+/* Keys per tile of the key sweep of the four-wavefront kernel for (d, dtype), or 0; for
+ * bf16 with d = 64 it is the tile of sweeps of at most 4096 keys (32), longer sweeps use
+ * 64-key tiles (attn_kernel_name names the instance a shape runs). */
 int attn_block_n(int d, attn_dtype dtype);
 
 /* Workgroups of the launch: B * H * ceil(Sq / block_m) * max(1, num_splits), or -1. */
